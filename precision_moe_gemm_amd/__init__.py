@@ -1,0 +1,287 @@
+"""precision_moe_gemm_amd -- Python binding of libnvfp4 (NVFP4 W4A4 on MI355X).
+
+Thin marshalling over the C ABI in include/nvfp4.h: torch tensors supply
+device memory and the current HIP stream, every computation runs in the
+library's gfx950 kernels.  Functions carry the C names.  A non-OK status
+raises :class:`NVFP4Error`.
+
+NVFP4 (page "Qwen3.8-Flash-Next-NVFP4", section 核心): E2M1 codes two per
+byte, one E4M3 scale per 16 elements along the last dimension, one FP32
+scale per tensor -- 4.5 bits per element.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
+    "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
+    "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_down", "nvfp4_moe_combine",
+    "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
+    "nvfp4_recipe", "status_string",
+]
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+def status_string(status: int) -> str:
+    return _lib.load().nvfp4_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != _lib.OK:
+        raise NVFP4Error(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libnvfp4 operates on device tensors")
+
+
+@dataclass
+class NVFP4Tensor:
+    """`batch` stacked NVFP4 matrices of rows x cols on one device.
+
+    packed uint8 [batch, rows, cols/2], scales uint8 (E4M3 bytes)
+    [batch, rows, cols/16], global float32 [batch]."""
+    packed: torch.Tensor
+    scales: torch.Tensor
+    global_: torch.Tensor
+    rows: int
+    cols: int
+    batch: int = 1
+
+    @staticmethod
+    def empty(rows: int, cols: int, batch: int = 1, device="cuda") -> "NVFP4Tensor":
+        return NVFP4Tensor(
+            torch.empty((batch, rows, cols // 2), dtype=torch.uint8, device=device),
+            torch.empty((batch, rows, cols // 16), dtype=torch.uint8, device=device),
+            torch.empty((batch,), dtype=torch.float32, device=device),
+            rows, cols, batch)
+
+    def c(self) -> _lib.NVFP4TensorC:
+        return _lib.NVFP4TensorC(self.packed.data_ptr(), self.scales.data_ptr(),
+                                 self.global_.data_ptr(), self.rows, self.cols, self.batch)
+
+    @property
+    def device(self):
+        return self.packed.device
+
+    def nbytes(self) -> int:
+        return self.packed.numel() + self.scales.numel() + 4 * self.global_.numel()
+
+
+def nvfp4_workspace_size(op: int, T: int = 0, k: int = 0, E: int = 0, H: int = 0, I: int = 0) -> int:
+    return int(_lib.load().nvfp4_workspace_size(op, T, k, E, H, I))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def nvfp4_recipe() -> list:
+    out = (ctypes.c_int32 * 6)()
+    _lib.load().nvfp4_recipe(out)
+    return list(out)
+
+
+def nvfp4_quantize(x: torch.Tensor, static_global: torch.Tensor | None = None,
+                   out: NVFP4Tensor | None = None, ws: torch.Tensor | None = None) -> NVFP4Tensor:
+    """bf16 [rows, cols] (row stride x.stride(0)) -> NVFP4."""
+    _need_cuda(x, static_global)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, 1, x.device)
+    if static_global is None and ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_QUANTIZE), x.device)
+    oc = out.c()
+    st = _lib.load().nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(static_global),
+                                   ctypes.byref(oc), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(x.device))
+    _check(st, "nvfp4_quantize")
+    return out
+
+
+def nvfp4_dequantize(t: NVFP4Tensor, dtype=torch.float32) -> torch.Tensor:
+    out = torch.empty((t.batch * t.rows, t.cols), dtype=dtype, device=t.device)
+    code = _lib.BF16 if dtype == torch.bfloat16 else _lib.F32
+    tc = t.c()
+    _check(_lib.load().nvfp4_dequantize(ctypes.byref(tc), _ptr(out), code, _stream(t.device)),
+           "nvfp4_dequantize")
+    return out
+
+
+def mxfp4_quantize(x: torch.Tensor):
+    """bf16 [rows, cols] -> (packed uint8 [rows, cols/2], e8m0 uint8 [rows, cols/32])."""
+    _need_cuda(x)
+    rows, cols = x.shape
+    packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    e8 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check(_lib.load().mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(packed), _ptr(e8),
+                                      _stream(x.device)), "mxfp4_quantize")
+    return packed, e8
+
+
+def mxfp4_to_nvfp4(packed: torch.Tensor, e8m0: torch.Tensor, rows: int, cols: int, batch: int = 1,
+                   out: NVFP4Tensor | None = None, ws: torch.Tensor | None = None,
+                   in_place: bool = False) -> NVFP4Tensor:
+    """Lossless remap of `batch` stacked MXFP4 matrices.  in_place=True makes
+    the result's codes alias `packed` (no copy)."""
+    _need_cuda(packed, e8m0)
+    dev = packed.device
+    if out is None:
+        if in_place:
+            out = NVFP4Tensor(packed.view(batch, rows, cols // 2),
+                              torch.empty((batch, rows, cols // 16), dtype=torch.uint8, device=dev),
+                              torch.empty((batch,), dtype=torch.float32, device=dev), rows, cols, batch)
+        else:
+            out = NVFP4Tensor.empty(rows, cols, batch, dev)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_REMAP, batch, 0, 0, rows, cols), dev)
+    oc = out.c()
+    _check(_lib.load().mxfp4_to_nvfp4(_ptr(packed), _ptr(e8m0), rows, cols, batch, ctypes.byref(oc),
+                                      _ptr(ws), ws.numel(), _stream(dev)), "mxfp4_to_nvfp4")
+    return out
+
+
+def nvfp4_gemm(A: NVFP4Tensor, W: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None):
+    """C[M, N] = A W^T with both operands NVFP4."""
+    if out is None:
+        out = torch.empty((A.rows, W.rows), dtype=dtype, device=A.device)
+    code = _lib.BF16 if out.dtype == torch.bfloat16 else _lib.F32
+    ac, wc = A.c(), W.c()
+    _check(_lib.load().nvfp4_gemm(ctypes.byref(ac), ctypes.byref(wc), _ptr(out), code,
+                                  _stream(A.device)), "nvfp4_gemm")
+    return out
+
+
+def nvfp4_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                           w13: NVFP4Tensor, w2: NVFP4Tensor, static_in_globals: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Routed-expert MoE forward: bf16 x [T, H] -> bf16 [T, H]."""
+    _need_cuda(x, topk_ids, topk_w)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E = w13.batch
+    I = w13.rows // 2
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE, T, k, E, H, I), x.device)
+    c13, c2 = w13.c(), w2.c()
+    _check(_lib.load().nvfp4_moe_grouped_gemm(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, E, ctypes.byref(c13), ctypes.byref(c2),
+        _ptr(static_in_globals), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
+        "nvfp4_moe_grouped_gemm")
+    return out
+
+
+def nvfp4_moe_route(topk_ids: torch.Tensor, E: int, ws: torch.Tensor | None = None):
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE_ROUTE, T, k, E), dev)
+    _check(_lib.load().nvfp4_moe_route(_ptr(topk_ids), T, k, E, _ptr(perm), _ptr(offsets), _ptr(inv),
+                                       _ptr(ws), ws.numel(), _stream(dev)), "nvfp4_moe_route")
+    return perm, offsets, inv
+
+
+def nvfp4_moe_gate_up(xq: NVFP4Tensor, perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                      w13: NVFP4Tensor, ws: torch.Tensor | None = None):
+    """h bf16 [T*k, I] (list order) and the uint32 max-|h| word."""
+    T = xq.rows
+    E = w13.batch
+    I = w13.rows // 2
+    dev = xq.device
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    hmax = torch.zeros(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE_ROUTE, T, k, E), dev)
+    xc, wc = xq.c(), w13.c()
+    _check(_lib.load().nvfp4_moe_gate_up(ctypes.byref(xc), _ptr(perm), _ptr(offsets), T, k, E,
+                                         ctypes.byref(wc), _ptr(h), _ptr(hmax), _ptr(ws), ws.numel(),
+                                         _stream(dev)), "nvfp4_moe_gate_up")
+    return h, hmax
+
+
+def nvfp4_moe_down(hq: NVFP4Tensor, offsets: torch.Tensor, T: int, k: int, w2: NVFP4Tensor,
+                   ws: torch.Tensor | None = None):
+    """y fp32 [T*k, H] (list order)."""
+    E = w2.batch
+    H = w2.rows
+    dev = hq.device
+    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE_ROUTE, T, k, E), dev)
+    hc, wc = hq.c(), w2.c()
+    _check(_lib.load().nvfp4_moe_down(ctypes.byref(hc), _ptr(offsets), T, k, E, ctypes.byref(wc),
+                                      _ptr(y), _ptr(ws), ws.numel(), _stream(dev)), "nvfp4_moe_down")
+    return y
+
+
+def nvfp4_moe_combine(y: torch.Tensor, inv: torch.Tensor, topk_w: torch.Tensor):
+    T, k = topk_w.shape
+    H = y.shape[1]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(_lib.load().nvfp4_moe_combine(_ptr(y), _ptr(inv), _ptr(topk_w), T, k, H, _ptr(out),
+                                         _stream(y.device)), "nvfp4_moe_combine")
+    return out
+
+
+def nvfp4_kv_quant(k: torch.Tensor | None, v: torch.Tensor | None, tok_offset: int,
+                   k_cache: NVFP4Tensor, v_cache: NVFP4Tensor, heads: int):
+    """Quantize bf16 [n, heads, head_dim] chunks into the caches at tok_offset."""
+    ref = k if k is not None else v
+    n = ref.shape[0]
+    kc, vc = k_cache.c(), v_cache.c()
+    _check(_lib.load().nvfp4_kv_quant(_ptr(k), _ptr(v), n, heads, tok_offset, ctypes.byref(kc),
+                                      ctypes.byref(vc), _stream(ref.device)), "nvfp4_kv_quant")
+
+
+def nvfp4_kv_dequant(k_cache: NVFP4Tensor, v_cache: NVFP4Tensor, heads: int, tok_begin: int, n: int,
+                     dtype=torch.bfloat16, want_k=True, want_v=True):
+    D = k_cache.cols
+    dev = k_cache.device
+    ko = torch.empty((n, heads, D), dtype=dtype, device=dev) if want_k else None
+    vo = torch.empty((n, heads, D), dtype=dtype, device=dev) if want_v else None
+    code = _lib.BF16 if dtype == torch.bfloat16 else _lib.F32
+    kc, vc = k_cache.c(), v_cache.c()
+    _check(_lib.load().nvfp4_kv_dequant(ctypes.byref(kc), ctypes.byref(vc), heads, tok_begin, n,
+                                        _ptr(ko), _ptr(vo), code, _stream(dev)), "nvfp4_kv_dequant")
+    return ko, vo
+
+
+def nvfp4_audit_scales(t: NVFP4Tensor) -> torch.Tensor:
+    """int64 [4] = {scale bytes, non-finite, non-positive, equal to 448}."""
+    counts = torch.empty(4, dtype=torch.int64, device=t.device)
+    tc = t.c()
+    _check(_lib.load().nvfp4_audit_scales(ctypes.byref(tc), _ptr(counts), _stream(t.device)),
+           "nvfp4_audit_scales")
+    return counts
+
+
+def nvfp4_get_error(device=None) -> int:
+    """Synchronize the current stream; return and clear the sticky device error."""
+    return int(_lib.load().nvfp4_get_error(_stream(device)))

@@ -1,0 +1,714 @@
+// libnvfp4.hip -- the C ABI of include/nvfp4.h: argument validation,
+// workspace layout and kernel dispatch.  One translation unit so that every
+// kernel shares the per-device sticky error word.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "common.h"
+#include "gemm.h"
+#include "moe.h"
+#include "mx.h"
+#include "quant.h"
+
+using namespace nvfp4;
+
+namespace {
+
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline nvfp4_status launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// grid for a grid-stride streaming kernel over `work` items of 256 threads
+inline unsigned stream_grid(int64_t work, int64_t cap = 8192)
+{
+    int64_t g = ceil_div(work, 256);
+    if (g < 1)
+        g = 1;
+    return (unsigned)std::min<int64_t>(g, cap);
+}
+
+// An empty tensor (rows or cols 0) may carry null code/scale pointers.
+nvfp4_status check_tensor(const nvfp4_tensor* t, bool need_global = true)
+{
+    if (!t || (need_global && !t->global))
+        return NVFP4_ERR_INVALID_ARG;
+    const bool empty = t->rows == 0 || t->cols == 0;
+    if (!empty && (!t->packed || !t->scales))
+        return NVFP4_ERR_INVALID_ARG;
+    if (t->rows < 0 || t->cols < 0 || t->batch < 1 || t->cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!aligned(t->packed, 16) || !aligned(t->scales, 4) || (t->global && !aligned(t->global, 4)))
+        return NVFP4_ERR_INVALID_ARG;
+    return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------- quantize
+// Launch the block quantizer for up to two tensors sharing a shape.
+nvfp4_status launch_quantize(QuantArgs a, int ntensors, hipStream_t st)
+{
+    const int64_t nblk = a.rows * a.blocks_per_row;
+    if (nblk == 0)
+        return NVFP4_OK;
+    dim3 grid(stream_grid(nblk, 4096), ntensors);
+    quantize_kernel<<<grid, kQuantThreads, 0, st>>>(a);
+    return launch_status();
+}
+
+nvfp4_status quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld, int src,
+                           const void* gsrc, const nvfp4_tensor* out, int64_t row_off,
+                           uint32_t* partials, hipStream_t st)
+{
+    QuantArgs a{};
+    a.x[0] = (const u32x4*)x;
+    a.packed[0] = (u32x2*)out->packed;
+    a.scales[0] = out->scales;
+    a.global_out[0] = out->global;
+    a.row_off[0] = row_off;
+    a.rows = rows;
+    a.blocks_per_row = cols / 16;
+    a.ld_chunks = ld / 8;
+    a.nparts = 0;
+    if (src == kGlobalPartials) {
+        const int64_t chunks = rows * (cols / 8);
+        const unsigned parts = stream_grid(chunks, kAmaxParts);
+        amax_partials_kernel<<<parts, kQuantThreads, 0, st>>>((const u32x4*)x, rows, cols / 8, ld / 8, partials);
+        nvfp4_status s = launch_status();
+        if (s != NVFP4_OK)
+            return s;
+        a.gsrc[0] = partials;
+        a.nparts = (int)parts;
+    } else {
+        a.gsrc[0] = gsrc;
+    }
+    a.src[0] = src;
+    if (rows == 0) {
+        // still publish G (1 for an empty dynamic tensor, or the static value)
+        a.rows = 1;
+        a.blocks_per_row = 0;
+        quantize_kernel<<<dim3(1, 1), kQuantThreads, 0, st>>>(a);
+        return launch_status();
+    }
+    return launch_quantize(a, 1, st);
+}
+
+// ---------------------------------------------------------------- GEMM
+template <int BM, int BN, int WM, int WN, int MODE>
+nvfp4_status launch_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
+{
+    p.m_tiles = m_tiles_ub;
+    int64_t blocks = m_tiles_ub * p.n_tiles;
+    if (blocks == 0)
+        return NVFP4_OK;
+    blocks = ceil_div(blocks, 8) * 8;
+    if (blocks > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    gemm_kernel<BM, BN, WM, WN, MODE><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(p);
+    return launch_status();
+}
+
+// Tile configurations: (BM, BN, waves).  Chosen by the rows an expert (or
+// the dense A) holds on average.
+template <int MODE>
+nvfp4_status dispatch_gemm(GemmArgs p, int64_t rows_avg, int64_t total_rows, int experts,
+                           int32_t* tile_off_ws, hipStream_t st)
+{
+    int bm;
+    if (rows_avg >= 256)
+        bm = 256;
+    else if (rows_avg >= 96)
+        bm = 128;
+    else if (rows_avg > 32)
+        bm = 64;
+    else
+        bm = 32;
+    const int bn = 256;
+    const int64_t ncols = (MODE == kModeGateUp) ? p.N : p.N;  // output columns
+    const int64_t per_tile_cols = (MODE == kModeGateUp) ? bn / 2 : bn;
+    p.n_tiles = ceil_div(ncols, per_tile_cols);
+    int64_t m_ub;
+    if (MODE == kModeDense) {
+        m_ub = ceil_div(total_rows, bm);
+    } else {
+        tile_offsets_kernel<<<1, 1024, 0, st>>>(p.offsets, experts, bm, tile_off_ws);
+        nvfp4_status s = launch_status();
+        if (s != NVFP4_OK)
+            return s;
+        p.tile_off = tile_off_ws;
+        m_ub = ceil_div(total_rows, bm) + experts;
+    }
+    switch (bm) {
+    case 256: return launch_gemm<256, 256, 2, 2, MODE>(p, m_ub, st);
+    case 128: return launch_gemm<128, 256, 2, 2, MODE>(p, m_ub, st);
+    case 64: return launch_gemm<64, 256, 1, 4, MODE>(p, m_ub, st);
+    default: return launch_gemm<32, 256, 1, 4, MODE>(p, m_ub, st);
+    }
+}
+
+// ---------------------------------------------------------------- MoE ws
+struct RouteLayout {
+    size_t hist, base, tot, offsets, tile_gu, tile_dn, end;
+};
+
+RouteLayout route_layout(int64_t npairs, int32_t E)
+{
+    RouteLayout L{};
+    const int64_t nchunks = std::max<int64_t>(1, ceil_div(npairs, kRouteChunk));
+    size_t o = 0;
+    L.hist = o; o = align256(o + sizeof(int32_t) * nchunks * E);
+    L.base = o; o = align256(o + sizeof(int32_t) * nchunks * E);
+    L.tot = o; o = align256(o + sizeof(int32_t) * E);
+    L.offsets = o; o = align256(o + sizeof(int32_t) * (E + 1));
+    L.tile_gu = o; o = align256(o + sizeof(int32_t) * (E + 1));
+    L.tile_dn = o; o = align256(o + sizeof(int32_t) * (E + 1));
+    L.end = o;
+    return L;
+}
+
+struct MoeLayout {
+    RouteLayout r;
+    size_t perm, inv, xparts, xq_p, xq_s, gx, h, hmax, hq_p, hq_s, gh, y, end;
+};
+
+MoeLayout moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
+{
+    MoeLayout L{};
+    const int64_t np = T * k;
+    L.r = route_layout(np, E);
+    size_t o = L.r.end;
+    L.perm = o; o = align256(o + sizeof(int32_t) * np);
+    L.inv = o; o = align256(o + sizeof(int32_t) * np);
+    L.xparts = o; o = align256(o + sizeof(uint32_t) * kAmaxParts);
+    L.xq_p = o; o = align256(o + (size_t)(T * H / 2));
+    L.xq_s = o; o = align256(o + (size_t)(T * H / 16));
+    L.gx = o; o = align256(o + sizeof(float));
+    L.h = o; o = align256(o + sizeof(uint16_t) * (size_t)(np * I));
+    L.hmax = o; o = align256(o + sizeof(uint32_t));
+    L.hq_p = o; o = align256(o + (size_t)(np * I / 2));
+    L.hq_s = o; o = align256(o + (size_t)(np * I / 16));
+    L.gh = o; o = align256(o + sizeof(float));
+    L.y = o; o = align256(o + sizeof(float) * (size_t)(np * H));
+    L.end = o;
+    return L;
+}
+
+template <typename T>
+inline T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+nvfp4_status route_impl(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
+                        int32_t* offsets, int32_t* inv, void* ws, const RouteLayout& L,
+                        uint32_t* zero_word, hipStream_t st)
+{
+    const int64_t np = T * k;
+    const int64_t nchunks = ceil_div(np, kRouteChunk);
+    if (np > 0) {
+        route_hist_kernel<<<(unsigned)nchunks, kRouteChunk, sizeof(int32_t) * E, st>>>(
+            ids, np, E, at<int32_t>(ws, L.hist));
+        route_expert_scan_kernel<<<(unsigned)E, 256, 0, st>>>(
+            at<int32_t>(ws, L.hist), nchunks, E, at<int32_t>(ws, L.base), at<int32_t>(ws, L.tot));
+    } else {
+        // no pairs: every expert is empty
+        fill_i32_kernel<<<stream_grid(E), 256, 0, st>>>(at<int32_t>(ws, L.tot), E, 0);
+    }
+    route_offsets_kernel<<<1, 1024, 0, st>>>(at<int32_t>(ws, L.tot), E, offsets, zero_word);
+    if (np > 0)
+        route_scatter_kernel<<<(unsigned)nchunks, kRouteChunk, 0, st>>>(
+            ids, np, E, at<int32_t>(ws, L.base), offsets, perm, inv);
+    return launch_status();
+}
+
+}  // namespace
+
+// ======================================================================== ABI
+
+extern "C" {
+
+const char* nvfp4_status_string(nvfp4_status s)
+{
+    switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_RANGE: return "value out of range";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_DEVICE: return "HIP device error";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported by this build";
+    }
+    return "unknown status";
+}
+
+void nvfp4_recipe(int32_t out[6])
+{
+    if (!out)
+        return;
+    out[0] = 16;   // block size
+    out[1] = 2;    // E2M1 exponent bits
+    out[2] = 1;    // E2M1 mantissa bits
+    out[3] = 4;    // E4M3 exponent bits
+    out[4] = 3;    // E4M3 mantissa bits
+    out[5] = 450;  // effective bits x 100: (16*4 + 8) / 16
+}
+
+size_t nvfp4_workspace_size(int op, int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
+{
+    switch (op) {
+    case NVFP4_OP_QUANTIZE:
+        return sizeof(uint32_t) * kAmaxParts;
+    case NVFP4_OP_REMAP: {
+        const int64_t batch = T < 1 ? 1 : T;
+        const int64_t blocks = H * (I / 32);
+        return align256((size_t)(batch * blocks)) + 2 * align256(sizeof(int) * kRemapParts * batch);
+    }
+    case NVFP4_OP_GEMM:
+        return 0;
+    case NVFP4_OP_MOE:
+        if (T < 0 || k < 1 || E < 1)
+            return 0;
+        return moe_layout(T, k, E, H, I).end;
+    case NVFP4_OP_MOE_ROUTE:
+        if (T < 0 || k < 1 || E < 1)
+            return 0;
+        return route_layout(T * k, E).end;
+    }
+    return 0;
+}
+
+nvfp4_status nvfp4_get_error(void* stream)
+{
+    if (hipStreamSynchronize(S(stream)) != hipSuccess)
+        return NVFP4_ERR_DEVICE;
+    unsigned v = 0, zero = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_nvfp4_error), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return NVFP4_ERR_DEVICE;
+    if (v != 0 && hipMemcpyToSymbol(HIP_SYMBOL(g_nvfp4_error), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) != hipSuccess)
+        return NVFP4_ERR_DEVICE;
+    return (nvfp4_status)v;
+}
+
+nvfp4_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                            const float* static_global, const nvfp4_tensor* out, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = check_tensor(out);
+    if (s != NVFP4_OK)
+        return s;
+    if ((!x && rows * cols != 0) || !aligned(x, 16))
+        return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || cols % 16 != 0 || ld < cols || ld % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (out->rows != rows || out->cols != cols || out->batch != 1)
+        return NVFP4_ERR_SHAPE;
+    if (static_global) {
+        if (!aligned(static_global, 4))
+            return NVFP4_ERR_INVALID_ARG;
+        return quantize_impl(x, rows, cols, ld, kGlobalStatic, static_global, out, 0, nullptr, S(stream));
+    }
+    if (!ws || !aligned(ws, 4))
+        return NVFP4_ERR_INVALID_ARG;
+    if (ws_bytes < nvfp4_workspace_size(NVFP4_OP_QUANTIZE, 0, 0, 0, 0, 0))
+        return NVFP4_ERR_WORKSPACE;
+    return quantize_impl(x, rows, cols, ld, kGlobalPartials, nullptr, out, 0, (uint32_t*)ws, S(stream));
+}
+
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dtype, void* stream)
+{
+    nvfp4_status s = check_tensor(in);
+    if (s != NVFP4_OK)
+        return s;
+    if (!out || !aligned(out, 16))
+        return NVFP4_ERR_INVALID_ARG;
+    if (dtype != NVFP4_F32 && dtype != NVFP4_BF16)
+        return NVFP4_ERR_INVALID_ARG;
+    const int64_t bpr = in->cols / 16;
+    const int64_t nblk = in->batch * in->rows * bpr;
+    if (nblk == 0 || in->rows == 0)
+        return NVFP4_OK;
+    const unsigned grid = stream_grid(nblk, 8192);
+    if (dtype == NVFP4_BF16)
+        dequantize_kernel<true><<<grid, kQuantThreads, 0, S(stream)>>>(
+            (const u32x2*)in->packed, in->scales, in->global, nblk, bpr, in->rows, 0, out);
+    else
+        dequantize_kernel<false><<<grid, kQuantThreads, 0, S(stream)>>>(
+            (const u32x2*)in->packed, in->scales, in->global, nblk, bpr, in->rows, 0, out);
+    return launch_status();
+}
+
+nvfp4_status mxfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* packed,
+                            uint8_t* e8m0, void* stream)
+{
+    if (!x || !packed || !e8m0 || !aligned(x, 16) || !aligned(packed, 16))
+        return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || ld < cols || ld % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    const int64_t bpr = cols / 32;
+    const int64_t nblk = rows * bpr;
+    if (nblk == 0)
+        return NVFP4_OK;
+    mxfp4_encode_kernel<<<stream_grid(nblk, 8192), kMxThreads, 0, S(stream)>>>(
+        (const u32x4*)x, rows, bpr, ld / 8, (u32x4*)packed, e8m0);
+    return launch_status();
+}
+
+nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0, int64_t rows, int64_t cols,
+                            int64_t batch, const nvfp4_tensor* out, void* ws, size_t ws_bytes,
+                            void* stream)
+{
+    nvfp4_status s = check_tensor(out);
+    if (s != NVFP4_OK)
+        return s;
+    if (!mx_packed || !e8m0 || !aligned(mx_packed, 16) || !ws || !aligned(ws, 4))
+        return NVFP4_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || batch < 1)
+        return NVFP4_ERR_SHAPE;
+    if (out->rows != rows || out->cols != cols || out->batch != batch)
+        return NVFP4_ERR_SHAPE;
+    if (ws_bytes < nvfp4_workspace_size(NVFP4_OP_REMAP, batch, 0, 0, rows, cols))
+        return NVFP4_ERR_WORKSPACE;
+    if (batch > 65535)
+        return NVFP4_ERR_UNSUPPORTED;
+    const int64_t per_mat = rows * (cols / 32);
+    uint8_t* flags = (uint8_t*)ws;
+    int* pmax = at<int>(ws, align256((size_t)(batch * per_mat)));
+    int* pmin = pmax + align256(sizeof(int) * kRemapParts * batch) / sizeof(int);
+    const unsigned parts = (unsigned)std::max<int64_t>(1, std::min<int64_t>(kRemapParts, ceil_div(per_mat, 256)));
+    u32x4* dst = (out->packed == mx_packed) ? nullptr : (u32x4*)out->packed;
+    remap_scan_kernel<<<dim3(parts, (unsigned)batch), kMxThreads, 0, S(stream)>>>(
+        (const u32x4*)mx_packed, e8m0, per_mat, dst, flags, pmax, pmin);
+    s = launch_status();
+    if (s != NVFP4_OK)
+        return s;
+    const unsigned parts2 = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, ceil_div(per_mat, 256)));
+    remap_scales_kernel<<<dim3(parts2, (unsigned)batch), kMxThreads, 0, S(stream)>>>(
+        e8m0, flags, per_mat, pmax, pmin, (int)parts, (uint16_t*)out->scales, out->global);
+    return launch_status();
+}
+
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, nvfp4_dtype dtype,
+                        void* stream)
+{
+    nvfp4_status s = check_tensor(A);
+    if (s == NVFP4_OK)
+        s = check_tensor(W);
+    if (s != NVFP4_OK)
+        return s;
+    if (!C || (dtype != NVFP4_F32 && dtype != NVFP4_BF16))
+        return NVFP4_ERR_INVALID_ARG;
+    if (A->cols != W->cols || A->batch != 1 || W->batch != 1)
+        return NVFP4_ERR_SHAPE;
+    if (A->cols % kBK != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (A->rows == 0 || W->rows == 0)
+        return NVFP4_OK;
+    if (A->cols == 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    GemmArgs p{};
+    p.a_packed = A->packed;
+    p.a_scales = A->scales;
+    p.a_global = A->global;
+    p.w_packed = W->packed;
+    p.w_scales = W->scales;
+    p.w_global = W->global;
+    p.K = A->cols;
+    p.M = A->rows;
+    p.N = W->rows;
+    p.experts = 1;
+    p.out = C;
+    p.out_bf16 = dtype == NVFP4_BF16;
+    return dispatch_gemm<kModeDense>(p, A->rows, A->rows, 1, nullptr, S(stream));
+}
+
+nvfp4_status nvfp4_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
+                             int32_t* offsets, int32_t* inv, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!ids || !perm || !offsets || !inv || !ws || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    const RouteLayout L = route_layout(T * k, E);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    return route_impl(ids, T, k, E, perm, offsets, inv, ws, L, nullptr, S(stream));
+}
+
+static nvfp4_status check_experts(const nvfp4_tensor* w13, const nvfp4_tensor* w2, int32_t E,
+                                  int64_t* H, int64_t* I)
+{
+    nvfp4_status s = NVFP4_OK;
+    if (w13) {
+        s = check_tensor(w13);
+        if (s != NVFP4_OK)
+            return s;
+        if (w13->batch != E || w13->rows % 2 != 0)
+            return NVFP4_ERR_SHAPE;
+        *H = w13->cols;
+        *I = w13->rows / 2;
+    }
+    if (w2) {
+        s = check_tensor(w2);
+        if (s != NVFP4_OK)
+            return s;
+        if (w2->batch != E)
+            return NVFP4_ERR_SHAPE;
+        if (w13 && (w2->rows != *H || w2->cols != *I))
+            return NVFP4_ERR_SHAPE;
+        *H = w2->rows;
+        *I = w2->cols;
+    }
+    return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+                               int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
+                               uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream)
+{
+    int64_t H = 0, I = 0;
+    nvfp4_status s = check_experts(w13, nullptr, E, &H, &I);
+    if (s == NVFP4_OK)
+        s = check_tensor(xq);
+    if (s != NVFP4_OK)
+        return s;
+    if (!perm || !offsets || !h || !h_amax || !ws || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || xq->rows != T || xq->cols != H || xq->batch != 1)
+        return NVFP4_ERR_SHAPE;
+    if (H % kBK != 0 || I % 128 != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    const RouteLayout L = route_layout(T * k, E);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    if (T == 0)
+        return NVFP4_OK;
+    GemmArgs p{};
+    p.a_packed = xq->packed;
+    p.a_scales = xq->scales;
+    p.a_global = xq->global;
+    p.w_packed = w13->packed;
+    p.w_scales = w13->scales;
+    p.w_global = w13->global;
+    p.K = H;
+    p.N = I;
+    p.offsets = offsets;
+    p.perm = perm;
+    p.topk = k;
+    p.experts = E;
+    p.out = h;
+    p.h_amax = h_amax;
+    return dispatch_gemm<kModeGateUp>(p, T * k / E, T * k, E, at<int32_t>(ws, L.tile_gu), S(stream));
+}
+
+nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
+                            int32_t E, const nvfp4_tensor* w2, float* y, void* ws, size_t ws_bytes,
+                            void* stream)
+{
+    int64_t H = 0, I = 0;
+    nvfp4_status s = check_experts(nullptr, w2, E, &H, &I);
+    if (s == NVFP4_OK)
+        s = check_tensor(hq);
+    if (s != NVFP4_OK)
+        return s;
+    if (!offsets || !y || !ws || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || hq->rows != T * k || hq->cols != I || hq->batch != 1)
+        return NVFP4_ERR_SHAPE;
+    if (I % kBK != 0 || H % 64 != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    const RouteLayout L = route_layout(T * k, E);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    if (T == 0)
+        return NVFP4_OK;
+    GemmArgs p{};
+    p.a_packed = hq->packed;
+    p.a_scales = hq->scales;
+    p.a_global = hq->global;
+    p.w_packed = w2->packed;
+    p.w_scales = w2->scales;
+    p.w_global = w2->global;
+    p.K = I;
+    p.N = H;
+    p.offsets = offsets;
+    p.topk = k;
+    p.experts = E;
+    p.out = y;
+    return dispatch_gemm<kModeDown>(p, T * k / E, T * k, E, at<int32_t>(ws, L.tile_dn), S(stream));
+}
+
+nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
+                               int64_t H, void* out, void* stream)
+{
+    if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 16))
+        return NVFP4_ERR_INVALID_ARG;
+    if (T < 0 || k < 1 || H < 0 || H % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (T == 0 || H == 0)
+        return NVFP4_OK;
+    combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, (u32x4*)out);
+    return launch_status();
+}
+
+nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const float* w, int64_t T,
+                                    int32_t k, int32_t E, const nvfp4_tensor* w13,
+                                    const nvfp4_tensor* w2, const float* static_in_globals, void* out,
+                                    void* ws, size_t ws_bytes, void* stream)
+{
+    int64_t H = 0, I = 0;
+    nvfp4_status s = check_experts(w13, w2, E, &H, &I);
+    if (s != NVFP4_OK)
+        return s;
+    if (!x || !ids || !w || !out || !ws || !aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    if (H % kBK != 0 || I % kBK != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    const MoeLayout L = moe_layout(T, k, E, H, I);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    if (T == 0)
+        return NVFP4_OK;
+    hipStream_t st = S(stream);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    int32_t* offsets = at<int32_t>(ws, L.r.offsets);
+    uint32_t* hmax = at<uint32_t>(ws, L.hmax);
+    // 1. route (also zeroes the h max word)
+    s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
+    if (s != NVFP4_OK)
+        return s;
+    // 2. quantize x once
+    nvfp4_tensor xq{at<uint8_t>(ws, L.xq_p), at<uint8_t>(ws, L.xq_s), at<float>(ws, L.gx), T, H, 1};
+    if (static_in_globals)
+        s = quantize_impl(x, T, H, H, kGlobalStatic, static_in_globals, &xq, 0, nullptr, st);
+    else
+        s = quantize_impl(x, T, H, H, kGlobalPartials, nullptr, &xq, 0, at<uint32_t>(ws, L.xparts), st);
+    if (s != NVFP4_OK)
+        return s;
+    // 3. gate_up + SwiGLU
+    void* h = at<void>(ws, L.h);
+    s = nvfp4_moe_gate_up(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, stream);
+    if (s != NVFP4_OK)
+        return s;
+    // 4. quantize h over all T*k rows
+    nvfp4_tensor hq{at<uint8_t>(ws, L.hq_p), at<uint8_t>(ws, L.hq_s), at<float>(ws, L.gh), T * k, I, 1};
+    if (static_in_globals)
+        s = quantize_impl(h, T * k, I, I, kGlobalStatic, static_in_globals + 1, &hq, 0, nullptr, st);
+    else
+        s = quantize_impl(h, T * k, I, I, kGlobalAmaxWord, hmax, &hq, 0, nullptr, st);
+    if (s != NVFP4_OK)
+        return s;
+    // 5. down
+    float* y = at<float>(ws, L.y);
+    s = nvfp4_moe_down(&hq, offsets, T, k, E, w2, y, ws, L.r.end, stream);
+    if (s != NVFP4_OK)
+        return s;
+    // 6. combine
+    return nvfp4_moe_combine(y, inv, w, T, k, H, out, stream);
+}
+
+nvfp4_status nvfp4_kv_quant(const void* k, const void* v, int64_t n, int64_t heads, int64_t tok_offset,
+                            const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache, void* stream)
+{
+    const void* src[2] = {k, v};
+    const nvfp4_tensor* dst[2] = {k_cache, v_cache};
+    QuantArgs a{};
+    int nt = 0;
+    int64_t D = -1;
+    if (n < 0 || heads < 1 || tok_offset < 0)
+        return NVFP4_ERR_SHAPE;
+    for (int j = 0; j < 2; j++) {
+        if (!src[j])
+            continue;
+        nvfp4_status s = check_tensor(dst[j]);
+        if (s != NVFP4_OK)
+            return s;
+        if (!aligned(src[j], 16))
+            return NVFP4_ERR_INVALID_ARG;
+        if (dst[j]->batch != 1 || dst[j]->rows % heads != 0 || (D >= 0 && dst[j]->cols != D))
+            return NVFP4_ERR_SHAPE;
+        D = dst[j]->cols;
+        if (D % 16 != 0 || (tok_offset + n) * heads > dst[j]->rows)
+            return NVFP4_ERR_SHAPE;
+        a.x[nt] = (const u32x4*)src[j];
+        a.packed[nt] = (u32x2*)dst[j]->packed;
+        a.scales[nt] = dst[j]->scales;
+        a.global_out[nt] = nullptr;
+        a.gsrc[nt] = dst[j]->global;
+        a.src[nt] = kGlobalStatic;
+        a.row_off[nt] = tok_offset * heads;
+        nt++;
+    }
+    if (nt == 0 || n == 0)
+        return NVFP4_OK;
+    a.rows = n * heads;
+    a.blocks_per_row = D / 16;
+    a.ld_chunks = D / 8;
+    return launch_quantize(a, nt, S(stream));
+}
+
+nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache, int64_t heads,
+                              int64_t tok_begin, int64_t n, void* k_out, void* v_out, nvfp4_dtype dtype,
+                              void* stream)
+{
+    const nvfp4_tensor* src[2] = {k_cache, v_cache};
+    void* dst[2] = {k_out, v_out};
+    if (n < 0 || heads < 1 || tok_begin < 0)
+        return NVFP4_ERR_SHAPE;
+    if (dtype != NVFP4_F32 && dtype != NVFP4_BF16)
+        return NVFP4_ERR_INVALID_ARG;
+    for (int j = 0; j < 2; j++) {
+        if (!dst[j])
+            continue;
+        nvfp4_status s = check_tensor(src[j]);
+        if (s != NVFP4_OK)
+            return s;
+        if (!aligned(dst[j], 16))
+            return NVFP4_ERR_INVALID_ARG;
+        if (src[j]->batch != 1 || src[j]->rows % heads != 0 || (tok_begin + n) * heads > src[j]->rows)
+            return NVFP4_ERR_SHAPE;
+    }
+    for (int j = 0; j < 2; j++) {
+        if (!dst[j] || n == 0)
+            continue;
+        const int64_t bpr = src[j]->cols / 16;
+        const int64_t nblk = n * heads * bpr;
+        const unsigned grid = stream_grid(nblk, 8192);
+        if (dtype == NVFP4_BF16)
+            dequantize_kernel<true><<<grid, kQuantThreads, 0, S(stream)>>>(
+                (const u32x2*)src[j]->packed, src[j]->scales, src[j]->global, nblk, bpr, src[j]->rows,
+                tok_begin * heads, dst[j]);
+        else
+            dequantize_kernel<false><<<grid, kQuantThreads, 0, S(stream)>>>(
+                (const u32x2*)src[j]->packed, src[j]->scales, src[j]->global, nblk, bpr, src[j]->rows,
+                tok_begin * heads, dst[j]);
+        nvfp4_status s = launch_status();
+        if (s != NVFP4_OK)
+            return s;
+    }
+    return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_audit_scales(const nvfp4_tensor* t, int64_t* counts, void* stream)
+{
+    nvfp4_status s = check_tensor(t, false);
+    if (s != NVFP4_OK)
+        return s;
+    if (!counts || !aligned(counts, 8))
+        return NVFP4_ERR_INVALID_ARG;
+    const int64_t n = t->batch * t->rows * (t->cols / 16);
+    zero_u64_kernel<<<1, 64, 0, S(stream)>>>((unsigned long long*)counts, 4);
+    if (n > 0)
+        audit_kernel<<<stream_grid(n, 1024), kQuantThreads, 0, S(stream)>>>(t->scales, n,
+                                                                             (unsigned long long*)counts);
+    return launch_status();
+}
+
+}  // extern "C"

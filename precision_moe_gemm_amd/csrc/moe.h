@@ -1,0 +1,199 @@
+// moe.h -- routed-expert plumbing around the grouped W4A4 GEMMs (page
+// "Qwen3.8-Flash-Next-NVFP4": routed experts with top-k routing and fused
+// gate_up / down projections; page "DeepSeek-V4.1-Flash-NVFP4", section 三:
+// experts w1, w3, w2).
+//
+// route: the T*k (token, slot) pairs p = t*k + j are listed expert by expert
+// and, inside an expert, in increasing p (a stable counting sort):
+//   1. per-chunk histograms (chunks of kRouteChunk pairs),
+//   2. per-expert scans turn them into per-chunk bases, then expert offsets,
+//   3. per-chunk stable scatter: a pair's rank among equal ids earlier in its
+//      chunk, plus its chunk base.
+// combine: out[t] = sum_j w[t,j] * y[inv[t*k+j]] in fp32, j ascending, one
+// thread per 8 output columns; no atomics, so results are run-to-run
+// identical.
+#pragma once
+#include "common.h"
+
+namespace nvfp4 {
+
+constexpr int kRouteChunk = 256;
+constexpr int kMaxExperts = 4096;
+
+// 1. hist[c][e] = pairs of chunk c routed to e.  Out-of-range ids raise the
+// sticky range error and are dropped.
+__global__ void __launch_bounds__(kRouteChunk)
+route_hist_kernel(const int32_t* __restrict__ ids, int64_t npairs, int E, int32_t* __restrict__ hist)
+{
+    extern __shared__ int32_t cnt[];  // [E]
+    for (int i = threadIdx.x; i < E; i += blockDim.x)
+        cnt[i] = 0;
+    __syncthreads();
+    const int64_t p = (int64_t)blockIdx.x * kRouteChunk + threadIdx.x;
+    if (p < npairs) {
+        const int32_t e = ids[p];
+        if (e >= 0 && e < E)
+            atomicAdd(&cnt[e], 1);
+        else
+            raise_error(NVFP4_ERR_RANGE);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += blockDim.x)
+        hist[(int64_t)blockIdx.x * E + i] = cnt[i];
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x <= 1024, a
+// multiple of 64).  Returns the exclusive prefix; *total gets the sum.
+NVFP4_DEV int32_t block_exclusive_scan(int32_t v, int32_t* lds16, int32_t* total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl += o;
+    }
+    __syncthreads();
+    if (lane == 63)
+        lds16[wid] = incl;
+    __syncthreads();
+    int32_t base = 0, all = 0;
+    const int nw = blockDim.x >> 6;
+    for (int w = 0; w < nw; w++) {
+        base += w < wid ? lds16[w] : 0;
+        all += lds16[w];
+    }
+    *total = all;
+    return base + incl - v;
+}
+
+// 2a. One workgroup per expert e: exclusive scan of hist[.][e] over chunks
+// into base[.][e]; tot[e] = pairs routed to e.
+__global__ void __launch_bounds__(256)
+route_expert_scan_kernel(const int32_t* __restrict__ hist, int64_t nchunks, int E,
+                         int32_t* __restrict__ base, int32_t* __restrict__ tot)
+{
+    __shared__ int32_t lds16[16];
+    const int e = blockIdx.x;
+    const int64_t per = (nchunks + blockDim.x - 1) / blockDim.x;
+    const int64_t c0 = threadIdx.x * per;
+    int32_t local = 0;
+    for (int64_t c = c0; c < c0 + per && c < nchunks; c++)
+        local += hist[c * E + e];
+    int32_t total;
+    int32_t run = block_exclusive_scan(local, lds16, &total);
+    for (int64_t c = c0; c < c0 + per && c < nchunks; c++) {
+        const int32_t v = hist[c * E + e];
+        base[c * E + e] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0)
+        tot[e] = total;
+}
+
+// 2b. One workgroup: offsets[e] = exclusive scan of tot, offsets[E] = total;
+// also zeroes `zero_word` (the h max word of the fused MoE) when given.
+__global__ void __launch_bounds__(1024)
+route_offsets_kernel(const int32_t* __restrict__ tot, int E, int32_t* __restrict__ offsets,
+                     uint32_t* zero_word)
+{
+    __shared__ int32_t lds16[16];
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per;
+    int32_t local = 0;
+    for (int e = e0; e < e0 + per && e < E; e++)
+        local += tot[e];
+    int32_t total;
+    int32_t run = block_exclusive_scan(local, lds16, &total);
+    for (int e = e0; e < e0 + per && e < E; e++) {
+        offsets[e] = run;
+        run += tot[e];
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = total;
+        if (zero_word)
+            *zero_word = 0;
+    }
+}
+
+// 3. Stable scatter of chunk c.
+__global__ void __launch_bounds__(kRouteChunk)
+route_scatter_kernel(const int32_t* __restrict__ ids, int64_t npairs, int E,
+                     const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+                     int32_t* __restrict__ perm, int32_t* __restrict__ inv)
+{
+    __shared__ int32_t sid[kRouteChunk];
+    const int64_t p = (int64_t)blockIdx.x * kRouteChunk + threadIdx.x;
+    const int32_t e = p < npairs ? ids[p] : -1;
+    sid[threadIdx.x] = e;
+    __syncthreads();
+    if (p >= npairs)
+        return;
+    if (e < 0 || e >= E) {
+        inv[p] = -1;
+        return;
+    }
+    int32_t rank = 0;
+    for (int i = 0; i < (int)threadIdx.x; i++)
+        rank += sid[i] == e;
+    const int32_t q = offsets[e] + base[(int64_t)blockIdx.x * E + e] + rank;
+    perm[q] = (int32_t)p;
+    inv[p] = q;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = v;
+}
+
+// m-tile prefix for a grouped GEMM with BM-row tiles:
+// tile_off[e] = sum_{e' < e} ceil(count_e' / BM).  One workgroup.
+__global__ void __launch_bounds__(1024)
+tile_offsets_kernel(const int32_t* __restrict__ offsets, int E, int bm, int32_t* __restrict__ tile_off)
+{
+    __shared__ int32_t lds16[16];
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per;
+    int32_t local = 0;
+    for (int e = e0; e < e0 + per && e < E; e++)
+        local += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    int32_t total;
+    int32_t run = block_exclusive_scan(local, lds16, &total);
+    for (int e = e0; e < e0 + per && e < E; e++) {
+        tile_off[e] = run;
+        run += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    }
+    if (threadIdx.x == 0)
+        tile_off[E] = total;
+}
+
+// out[t, 8c..8c+8) = bf16(sum_j w[t,j] * y[inv[t*k+j], 8c..8c+8))
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
+               const float* __restrict__ w, int64_t T, int k, int64_t H, u32x4* __restrict__ out)
+{
+    const int64_t groups = H / 8;
+    const int64_t total = T * groups;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t t = i / groups, c = i - t * groups;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < k; j++) {
+            const int32_t q = inv[t * k + j];
+            if (q < 0)
+                continue;
+            const float wt = w[t * k + j];
+            const float4_t* src = (const float4_t*)(y + (int64_t)q * H + 8 * c);
+            const float4_t v0 = src[0], v1 = src[1];
+            acc[0] += wt * v0.x; acc[1] += wt * v0.y; acc[2] += wt * v0.z; acc[3] += wt * v0.w;
+            acc[4] += wt * v1.x; acc[5] += wt * v1.y; acc[6] += wt * v1.z; acc[7] += wt * v1.w;
+        }
+        out[i] = (u32x4){pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    }
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,104 @@
+"""GPU parity: dense W4A4 GEMM vs the exact (int64) oracle.
+
+Bar: max|C - R| / max|R| <= 1e-3 (fp32 accumulation order) for fp32 output,
+1e-3 + 2^-8 for bf16 output; bit-exact in the integer special case (all
+scales 1, G = 1, where every partial sum is a small integer).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_moe_gemm_amd as nv
+from precision_moe_gemm_amd import synth
+from tests.gpu_util import BF16_HALF_ULP, GEMM_TOL, assert_same_nvfp4, rel_err, step, to_oracle, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _q(t):
+    return nv.nvfp4_quantize(t.to(DEV) if not t.is_cuda else t)
+
+
+def test_tiny_linear(orc):
+    x, w = synth.C1.x(), synth.C1.w()
+    step("gemm tiny linear 16x256x512")
+    A, W = _q(x), _q(w)
+    Ao, Wo = orc.quantize(synth.bits(x)), orc.quantize(synth.bits(w))
+    assert_same_nvfp4(A, Ao)
+    assert_same_nvfp4(W, Wo)
+    C = nv.nvfp4_gemm(A, W).cpu().numpy()
+    R = orc.gemm(Ao, Wo)
+    err = rel_err(C, R)
+    print(f"tiny linear rel err {err:.3e}")
+    assert err <= GEMM_TOL
+    Cb = nv.nvfp4_gemm(A, W, torch.bfloat16).float().cpu().numpy()
+    assert rel_err(Cb, R) <= GEMM_TOL + BF16_HALF_ULP
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (5, 300, 256), (33, 512, 640), (100, 256, 1152),
+                                   (129, 768, 512), (300, 256, 256), (517, 1280, 384)])
+def test_random_shapes(orc, M, N, K):
+    x = synth.normal_bf16((M, K), 1.0, (300, M, K))
+    w = synth.normal_bf16((N, K), 0.02, (301, N, K))
+    step(f"gemm random M={M} N={N} K={K}")
+    A, W = _q(x), _q(w)
+    C = nv.nvfp4_gemm(A, W).cpu().numpy()
+    R = orc.gemm(to_oracle(A), to_oracle(W))
+    assert rel_err(C, R) <= GEMM_TOL
+
+
+def test_integer_special_case_is_exact(orc):
+    rng = np.random.default_rng(4)
+    M, N, K = 64, 512, 1024
+    a = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    w = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    one = lambda r: np.full((r, K // 16), 0x38, np.uint8)
+    A = nv.NVFP4Tensor(torch.from_numpy(a[None]).to(DEV), torch.from_numpy(one(M)[None]).to(DEV),
+                       torch.ones(1, device=DEV), M, K)
+    W = nv.NVFP4Tensor(torch.from_numpy(w[None]).to(DEV), torch.from_numpy(one(N)[None]).to(DEV),
+                       torch.ones(1, device=DEV), N, K)
+    step("gemm integer special case")
+    C = nv.nvfp4_gemm(A, W).cpu().numpy().astype(np.float64)
+    R = orc.gemm(orc.NVFP4(a, one(M), 1.0), orc.NVFP4(w, one(N), 1.0))
+    np.testing.assert_array_equal(C, R)
+
+
+@pytest.mark.parametrize("M", [1, 32, 8192])
+def test_dense_mlp_gate_up_sampled(orc, M):
+    """27B-class gate_up projection (34816 x 5120) at its real shape; the oracle
+    computes sampled output rows and columns one by one."""
+    c = synth.C2
+    w = c.w13(DEV)
+    W = nv.nvfp4_quantize(w)
+    x = c.x(M, DEV)
+    A = nv.nvfp4_quantize(x)
+    step(f"gemm dense MLP gate_up M={M}")
+    C = nv.nvfp4_gemm(A, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.r_[rng.choice(M, min(M, 6), replace=False), M - 1])
+    cols = np.unique(np.r_[rng.choice(w.shape[0], 96, replace=False), 0, w.shape[0] - 1])
+    Ao = to_oracle(A)
+    Wo = orc.NVFP4(u8(W.packed)[0][cols], u8(W.scales)[0][cols], W.global_.item())
+    R = orc.gemm_rows(Ao, Wo, a_rows=rows)
+    got = C.cpu().numpy()[np.ix_(rows, cols)]
+    err = rel_err(got, R)
+    print(f"dense MLP M={M} sampled rel err {err:.3e}")
+    assert err <= GEMM_TOL
+    del w, W, C
+
+
+def test_unsupported_k():
+    A = nv.NVFP4Tensor.empty(4, 80, 1, DEV)
+    W = nv.NVFP4Tensor.empty(8, 80, 1, DEV)
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.nvfp4_gemm(A, W)
+    assert ei.value.status == 6
+
+
+def test_gemm_deterministic():
+    x, w = synth.C1.x(DEV), synth.C1.w(DEV)
+    A, W = nv.nvfp4_quantize(x), nv.nvfp4_quantize(w)
+    assert torch.equal(nv.nvfp4_gemm(A, W), nv.nvfp4_gemm(A, W))
