@@ -545,12 +545,12 @@ nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int6
 nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
                                int64_t H, void* out, void* stream)
 {
-    if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 16))
-        return NVFP4_ERR_INVALID_ARG;
     if (T < 0 || k < 1 || H < 0 || H % 8 != 0)
         return NVFP4_ERR_SHAPE;
     if (T == 0 || H == 0)
         return NVFP4_OK;
+    if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 16))
+        return NVFP4_ERR_INVALID_ARG;
     combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, (u32x4*)out);
     return launch_status();
 }
@@ -564,17 +564,17 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     nvfp4_status s = check_experts(w13, w2, E, &H, &I);
     if (s != NVFP4_OK)
         return s;
-    if (!x || !ids || !w || !out || !ws || !aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256))
-        return NVFP4_ERR_INVALID_ARG;
     if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
     if (H % kBK != 0 || I % kBK != 0)
         return NVFP4_ERR_UNSUPPORTED;
+    if (T == 0)
+        return NVFP4_OK;
+    if (!x || !ids || !w || !out || !ws || !aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
     const MoeLayout L = moe_layout(T, k, E, H, I);
     if (ws_bytes < L.end)
         return NVFP4_ERR_WORKSPACE;
-    if (T == 0)
-        return NVFP4_OK;
     hipStream_t st = S(stream);
     int32_t* perm = at<int32_t>(ws, L.perm);
     int32_t* inv = at<int32_t>(ws, L.inv);

@@ -1,0 +1,222 @@
+"""GPU parity: routed-expert MoE (route, gate_up + SwiGLU, h quantize, down,
+combine) vs the oracle, following the staged protocol:
+
+  1. x and every weight: GPU bytes bit-exact vs oracle Q (then the oracle uses
+     its own, identical, quantized operands);
+  2. route: perm / offsets / inv bit-exact;
+  3. h: GPU gate_up output vs the oracle's h on the same quantized operands,
+     max|h - R| / max|R| <= 1e-3 + 2^-8 (bf16 output);
+  4. G_h == amax(h_gpu) / 2688 exactly, oracle Q(h_gpu) == GPU hq bit-exact;
+  5. y: GPU down output vs the oracle on GPU hq, <= 1e-3;
+  6. out: GPU combine vs the oracle's combine of the oracle y, <= 1e-3 + 2^-8;
+  7. the fused entry point equals the staged one bit for bit.
+End-to-end oracle error (h re-quantization amplifies fp32 order
+differences) is printed, gated only loosely.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_moe_gemm_amd as nv
+from precision_moe_gemm_amd import synth, workloads
+from tests.gpu_util import (BF16_HALF_ULP, GEMM_TOL, bf16_to_f64, rel_err, step, tensor_bf16_to_f64,
+                            to_oracle, u8)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle_expert_checked(orc, W, cfg, e, which):
+    """Oracle Q of expert e's bf16 weights, checked bit-exact against the GPU copy."""
+    if which == "w13":
+        src = synth.bits(cfg.w13(e, DEV))
+        gt = workloads.expert_view(W.w13, e)
+    else:
+        src = synth.bits(cfg.w2(e, DEV))
+        gt = workloads.expert_view(W.w2, e)
+    if cfg.mx:
+        ref = orc.mxfp4_to_nvfp4(*orc.mxfp4_encode(src))
+    else:
+        ref = orc.quantize(src)
+    np.testing.assert_array_equal(u8(gt.scales)[0], ref.scales)
+    np.testing.assert_array_equal(u8(gt.packed)[0], ref.packed)
+    assert np.float32(gt.global_.item()) == ref.G
+    return ref
+
+
+def _run_staged(x, ids, w, W, cfg):
+    T, k, E = cfg.T, cfg.k, cfg.E
+    xq = nv.nvfp4_quantize(x)
+    perm, offsets, inv = nv.nvfp4_moe_route(ids, E)
+    h, hmax = nv.nvfp4_moe_gate_up(xq, perm, offsets, k, W.w13)
+    hq = nv.nvfp4_quantize(h)
+    y = nv.nvfp4_moe_down(hq, offsets, T, k, W.w2)
+    out = nv.nvfp4_moe_combine(y, inv, w)
+    torch.cuda.synchronize()
+    return dict(xq=xq, perm=perm, offsets=offsets, inv=inv, h=h, hmax=hmax, hq=hq, y=y, out=out)
+
+
+def _check_moe(orc, cfg, sample_rows=None, sample_tokens=None, seed=0):
+    step(f"moe build E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} T={cfg.T} mx={cfg.mx}")
+    W = workloads.build_moe_weights(cfg, DEV)
+    x = cfg.x(DEV)
+    ids, w = workloads.routing(cfg, DEV)
+    step("moe staged run")
+    g = _run_staged(x, ids, w, W, cfg)
+    T, k, E = cfg.T, cfg.k, cfg.E
+    ids_np = ids.cpu().numpy()
+    w_np = w.cpu().numpy()
+    # 1. x bit-exact
+    xo = orc.quantize(synth.bits(x))
+    np.testing.assert_array_equal(u8(g["xq"].scales)[0], xo.scales)
+    np.testing.assert_array_equal(u8(g["xq"].packed)[0], xo.packed)
+    assert np.float32(g["xq"].global_.item()) == xo.G
+    # 2. route bit-exact
+    perm, offsets, inv = orc.moe_route(ids_np, E)
+    np.testing.assert_array_equal(g["perm"].cpu().numpy(), perm)
+    np.testing.assert_array_equal(g["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(g["inv"].cpu().numpy(), inv)
+    rng = np.random.default_rng(seed)
+    npairs = T * k
+    if sample_rows is None:
+        rows = np.arange(npairs)
+    else:
+        rows = np.unique(np.r_[rng.choice(npairs, sample_rows, replace=False), 0, npairs - 1])
+    experts_needed = sorted(set(int(np.searchsorted(offsets, q, side="right") - 1) for q in rows))
+    # oracle expert operands (bit-exact vs GPU), others zero-filled (never read)
+    H, I = cfg.H, cfg.I
+    w13p = np.zeros((E, 2 * I, H // 2), np.uint8)
+    w13s = np.zeros((E, 2 * I, H // 16), np.uint8)
+    w13g = np.ones(E, np.float32)
+    w2p = np.zeros((E, H, I // 2), np.uint8)
+    w2s = np.zeros((E, H, I // 16), np.uint8)
+    w2g = np.ones(E, np.float32)
+    for e in experts_needed:
+        r13 = _oracle_expert_checked(orc, W, cfg, e, "w13")
+        w13p[e], w13s[e], w13g[e] = r13.packed, r13.scales, r13.G
+        r2 = _oracle_expert_checked(orc, W, cfg, e, "w2")
+        w2p[e], w2s[e], w2g[e] = r2.packed, r2.scales, r2.G
+    ex13 = orc.Experts(w13p, w13s, w13g)
+    ex2 = orc.Experts(w2p, w2s, w2g)
+    # 3. h on sampled list positions
+    h_ref = orc.moe_gate_up(xo, perm, offsets, k, ex13, rows)
+    h_gpu = g["h"].cpu()
+    h_bits = synth.bits(h_gpu)
+    err_h = rel_err(bf16_to_f64(h_bits[rows]), bf16_to_f64(h_ref))
+    print(f"h rel err {err_h:.3e}")
+    assert err_h <= GEMM_TOL + BF16_HALF_ULP
+    # 4. G_h and hq bit-exact vs oracle Q(h_gpu)
+    amax_h = np.abs(bf16_to_f64(h_bits)).max()
+    assert np.uint32(g["hmax"].item()) == np.float32(amax_h).view(np.uint32)
+    hq_ref = orc.quantize(np.ascontiguousarray(h_bits[rows]), static_G=orc.global_from_amax(amax_h))
+    assert np.float32(g["hq"].global_.item()) == np.float32(orc.global_from_amax(amax_h))
+    np.testing.assert_array_equal(u8(g["hq"].scales)[0][rows], hq_ref.scales)
+    np.testing.assert_array_equal(u8(g["hq"].packed)[0][rows], hq_ref.packed)
+    # 5. y from the GPU's hq
+    hq_full = to_oracle(g["hq"])
+    y_ref = orc.moe_down(hq_full, offsets, ex2, rows)
+    err_y = rel_err(g["y"].cpu().numpy()[rows], y_ref)
+    print(f"y rel err {err_y:.3e}")
+    assert err_y <= GEMM_TOL
+    # 6. combine on sampled tokens (all k slots of each)
+    if sample_tokens is None:
+        toks = np.arange(T)
+    else:
+        toks = np.unique(np.r_[rng.choice(T, sample_tokens, replace=False), T - 1])
+    slot_rows = inv.reshape(T, k)[toks].ravel()
+    for e in sorted(set(int(np.searchsorted(offsets, q, side="right") - 1) for q in slot_rows)):
+        if e not in experts_needed:
+            r2 = _oracle_expert_checked(orc, W, cfg, e, "w2")
+            w2p[e], w2s[e], w2g[e] = r2.packed, r2.scales, r2.G
+    ex2 = orc.Experts(w2p, w2s, w2g)
+    y_tok = orc.moe_down(hq_full, offsets, ex2, slot_rows)
+    y_full = np.zeros((T * k, H))
+    y_full[slot_rows] = y_tok
+    out_ref = orc.moe_combine(y_full, inv, w_np)[toks]
+    err_o = rel_err(tensor_bf16_to_f64(g["out"])[toks], bf16_to_f64(out_ref))
+    print(f"out rel err {err_o:.3e}")
+    assert err_o <= GEMM_TOL + BF16_HALF_ULP
+    # 7. fused == staged
+    step("moe fused run")
+    fused = nv.nvfp4_moe_grouped_gemm(x, ids, w, W.w13, W.w2)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, g["out"])
+    assert nv.nvfp4_get_error() == 0
+    return g, W
+
+
+def test_small_moe_every_row(orc):
+    cfg = synth.MoE(seed=30, E=8, k=3, H=512, I=256, T=77)
+    _check_moe(orc, cfg)
+
+
+def test_small_moe_mx_experts_every_row(orc):
+    cfg = synth.MoE(seed=31, E=5, k=2, H=384, I=256, T=50, zipf=1.1, mx=True)
+    _check_moe(orc, cfg)
+
+
+def test_moe_512_experts_top10_sampled(orc):
+    """512 experts, top-10, T=4096, H=4096, I=1024 at full size."""
+    _check_moe(orc, synth.C3, sample_rows=24, sample_tokens=6)
+
+
+def test_moe_384_experts_decode_sampled(orc):
+    """384 MXFP4-origin experts, top-8, H=7168, I=2048, T=64 (decode batch)."""
+    _check_moe(orc, synth.C4_DECODE, sample_rows=24, sample_tokens=6)
+
+
+def test_single_expert_is_dense_mlp(orc):
+    """E=1, k=1, w=1: the MoE path equals the dense MLP built from nvfp4_gemm."""
+    T, H, I = 40, 512, 384
+    x = synth.normal_bf16((T, H), 1.0, (32, 0), DEV)
+    w13 = nv.nvfp4_quantize(synth.normal_bf16((2 * I, H), 0.02, (32, 1), DEV))
+    w2 = nv.nvfp4_quantize(synth.normal_bf16((H, I), 0.02, (32, 2), DEV))
+    ids = torch.zeros((T, 1), dtype=torch.int32, device=DEV)
+    wt = torch.ones((T, 1), dtype=torch.float32, device=DEV)
+    step("moe E=1 vs dense")
+    out = nv.nvfp4_moe_grouped_gemm(x, ids, wt, w13, w2)
+    xq = nv.nvfp4_quantize(x)
+    gu = nv.nvfp4_gemm(xq, w13)
+    h = (torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]).to(torch.bfloat16)
+    ref = nv.nvfp4_gemm(nv.nvfp4_quantize(h), w2, torch.bfloat16)
+    err = rel_err(out.float().cpu().numpy(), ref.float().cpu().numpy())
+    print(f"E=1 MoE vs dense rel err {err:.3e}")
+    assert err <= 2e-2  # h re-quantization can flip codes between the two fp32 orders
+
+
+def test_invalid_expert_ids_raise_and_are_dropped(orc):
+    T, k, E = 20, 2, 4
+    ids = torch.randint(0, E, (T, k), dtype=torch.int32, device=DEV)
+    ids[3, 1] = 7
+    ids[5, 0] = -1
+    step("route with invalid ids")
+    perm, offsets, inv = nv.nvfp4_moe_route(ids, E)
+    assert nv.nvfp4_get_error() == 3
+    inv = inv.cpu().numpy()
+    assert inv[3 * k + 1] == -1 and inv[5 * k + 0] == -1
+    assert offsets.cpu().numpy()[E] == T * k - 2
+    assert nv.nvfp4_get_error() == 0
+
+
+def test_moe_empty_and_deterministic():
+    cfg = synth.MoE(seed=33, E=4, k=2, H=256, I=128, T=16)
+    W = workloads.build_moe_weights(cfg, DEV)
+    x = cfg.x(DEV)
+    ids, w = workloads.routing(cfg, DEV)
+    a = nv.nvfp4_moe_grouped_gemm(x, ids, w, W.w13, W.w2)
+    b = nv.nvfp4_moe_grouped_gemm(x, ids, w, W.w13, W.w2)
+    assert torch.equal(a, b)
+    e = nv.nvfp4_moe_grouped_gemm(x[:0], ids[:0], w[:0], W.w13, W.w2)
+    assert e.shape == (0, cfg.H)
+
+
+def test_static_globals_equal_dynamic():
+    cfg = synth.MoE(seed=34, E=4, k=2, H=256, I=128, T=33)
+    W = workloads.build_moe_weights(cfg, DEV)
+    x = cfg.x(DEV)
+    ids, w = workloads.routing(cfg, DEV)
+    g = _run_staged(x, ids, w, W, cfg)
+    sg = torch.stack([g["xq"].global_[0], g["hq"].global_[0]]).contiguous()
+    out = nv.nvfp4_moe_grouped_gemm(x, ids, w, W.w13, W.w2, static_in_globals=sg)
+    assert torch.equal(out, g["out"])
