@@ -90,7 +90,9 @@ enum {
 };
 
 /* Bytes of `ws` an operation needs.  Unused arguments may be 0:
- *   QUANTIZE: none.  REMAP: T = batch, H = rows, I = cols.  GEMM: none.
+ *   QUANTIZE: none.  REMAP: T = batch, H = rows, I = cols.
+ *   GEMM: T = M (rows of A), H = K, I = N (rows of W); non-zero only for
+ *         few-row shapes whose K is split over several workgroups.
  *   MOE, MOE_ROUTE: T tokens, k slots, E experts, H hidden, I intermediate. */
 size_t nvfp4_workspace_size(int op, int64_t T, int32_t k, int32_t E, int64_t H, int64_t I);
 
@@ -159,10 +161,16 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0,
  *   C[m, n] = G_A * G_W * sum_k (e2m1*s)(A[m,k]) * (e2m1*s)(W[n,k])
  * A: [M, K] (batch 1), W: [N, K] (batch 1); C: [M, N] row-major, fp32 or
  * bf16.  Products are exact; the sum is accumulated in fp32.
- * K % 16 == 0 (K % 128 == 0 on this build, else NVFP4_ERR_UNSUPPORTED).
+ * K % 16 == 0 (K % 64 == 0 on this build, else NVFP4_ERR_UNSUPPORTED).
+ * ws: nvfp4_workspace_size(NVFP4_OP_GEMM, M, 0, 0, K, N) bytes, 256-byte
+ *     aligned, holding the fp32 partial sums of few-row shapes whose K is
+ *     split over several workgroups (they are added in a fixed order, so
+ *     results are reproducible).  NULL (or a size of 0) is allowed: the
+ *     GEMM then runs unsplit, slower for such shapes.  A non-NULL ws that is
+ *     smaller than required gives NVFP4_ERR_WORKSPACE.
  */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, nvfp4_dtype dtype,
-                        void* stream);
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Routed-expert MoE layer with NVFP4 experts (page "Qwen3.8-Flash-Next-NVFP4":
@@ -183,7 +191,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
  * the pair is dropped); topk_w fp32 [T, k]; x bf16 [T, H] contiguous;
  * w13: batch E, rows 2I, cols H; w2: batch E, rows H, cols I;
  * static_in_globals: device float[2] or NULL; out bf16 [T, H].
- * H % 128 == 0 and I % 128 == 0 on this build (else NVFP4_ERR_UNSUPPORTED).
+ * H % 64 == 0 and I % 128 == 0 on this build (else NVFP4_ERR_UNSUPPORTED).
  * ws: nvfp4_workspace_size(NVFP4_OP_MOE, T, k, E, H, I) bytes.
  */
 nvfp4_status nvfp4_moe_grouped_gemm(const void* x_bf16, const int32_t* topk_ids,

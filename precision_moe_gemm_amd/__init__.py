@@ -163,14 +163,19 @@ def mxfp4_to_nvfp4(packed: torch.Tensor, e8m0: torch.Tensor, rows: int, cols: in
     return out
 
 
-def nvfp4_gemm(A: NVFP4Tensor, W: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None):
-    """C[M, N] = A W^T with both operands NVFP4."""
+def nvfp4_gemm(A: NVFP4Tensor, W: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None):
+    """C[M, N] = A W^T with both operands NVFP4.  `ws` (uint8, 256-byte
+    aligned) holds split-K partials of few-row shapes; allocated if omitted."""
     if out is None:
         out = torch.empty((A.rows, W.rows), dtype=dtype, device=A.device)
     code = _lib.BF16 if out.dtype == torch.bfloat16 else _lib.F32
+    if ws is None:
+        n = nvfp4_workspace_size(_lib.OP_GEMM, A.rows, 0, 0, A.cols, W.rows)
+        ws = _workspace(n, A.device) if n else None
     ac, wc = A.c(), W.c()
-    _check(_lib.load().nvfp4_gemm(ctypes.byref(ac), ctypes.byref(wc), _ptr(out), code,
-                                  _stream(A.device)), "nvfp4_gemm")
+    _check(_lib.load().nvfp4_gemm(ctypes.byref(ac), ctypes.byref(wc), _ptr(out), code, _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(A.device)), "nvfp4_gemm")
     return out
 
 

@@ -8,29 +8,30 @@
 //
 // Mapping onto CDNA4.  gfx950's scaled FP4 MFMA takes one power-of-two scale
 // per 32 elements, NVFP4 needs an E4M3 scale (3 mantissa bits) per 16, so
-// NVFP4 does not map onto it.  Instead every element is decoded to f16: the
-// E2M1 value q (1 cvt per 2 elements, exact) times the E4M3 scale s (one
-// packed f16 multiply per 2 elements).  q*s has at most 6 significant bits
-// and lies in [2^-10, 2688], so it is exact in f16, the MFMA products are
-// exact in fp32 and only the fp32 summation rounds.
+// NVFP4 does not map onto it.  Every element is decoded to f16 instead: the
+// fp4->f16 conversion instruction (full VALU rate, 2 codes per instruction,
+// unit scale) gives each E2M1 value q exactly, and one packed f16 multiply by
+// the E4M3 scale s gives q*s exactly (at most 6 significant bits, magnitude
+// in [2^-10, 2688], inside the f16 normal range).  Products are exact in fp32,
+// only the fp32 summation rounds, and the epilogue multiplies by G_A * G_W.
 //
-// Tiling.  A workgroup of WM x WN waves owns a BM x BN output tile and walks
-// K in stages of 128 elements.  Each stage stages the *packed* operands in
-// LDS (64 bytes of codes + 8 scale bytes per row, double-buffered), so LDS
-// traffic is a quarter of an f16 tile.  Each wave reads its fragments'
-// codes from LDS, decodes them in registers and issues
-// v_mfma_f32_32x32x16_f16.  Inside a stage the K order is permuted: the two
-// 32-lane halves of a wave hold elements [0, 64) and [64, 128) of the stage
-// and step through them 8 at a time; A and W use the same permutation, which
-// leaves the sum unchanged and lets every lane read 16 contiguous bytes.
+// Tiling.  A workgroup of 4 waves (WM x WN) owns a BM x BN output tile and
+// walks K in stages of 64.  Each element of a stage is decoded once per
+// workgroup: thread t loads the packed codes and scale bytes of one A row and
+// one W row (registers, prefetched a stage ahead), decodes them and writes
+// f16 into a double-buffered LDS tile (rows of 128 bytes, 16-byte chunks
+// XOR-swizzled by row so fragment reads and decode writes are free of bank
+// conflicts).  Waves read MFMA fragments (8 f16 per lane) from the current
+// tile and issue v_mfma_f32_32x32x16_f16 while decoding the next stage.
 #pragma once
 #include "common.h"
 
 namespace nvfp4 {
 
-constexpr int kBK = 128;          // K elements per stage
-constexpr int kRowBytes = kBK / 2; // packed bytes per row per stage
-constexpr int kRowScales = kBK / 16;
+constexpr int kBK = 64;             // K elements per stage
+constexpr int kRowF16Bytes = kBK * 2;  // f16 bytes per tile row per stage
+constexpr int kStageCodeBytes = kBK / 2;
+constexpr int kStageScaleBytes = kBK / 16;
 
 enum GemmMode : int {
     kModeDense = 0,   // C = acc * G_A * G_W  (fp32 or bf16 output)
@@ -61,20 +62,14 @@ struct GemmArgs {
     void* out;                // dense: C; gate_up: h bf16 [T*k, I]; down: y fp32
     int out_bf16;             // dense only
     uint32_t* h_amax;         // gate_up only
+    // weight-streaming kernel, dense mode: K split over `ksplit` workgroups
+    // whose raw fp32 sums go to partial[ksplit][M][N] (ksplit > 1 only)
+    int32_t ksplit;
+    float* partial;
 };
 
-NVFP4_DEV int lds_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-
-// Eight E2M1 codes (one dword) times one f16 scale -> the MFMA operand.
-NVFP4_DEV half8_t decode8(uint32_t codes, _Float16 s)
-{
-    const half2_t ss = {s, s};
-    const half2_t h0 = FP4_TO_F16X2(codes, 0) * ss;
-    const half2_t h1 = FP4_TO_F16X2(codes, 1) * ss;
-    const half2_t h2 = FP4_TO_F16X2(codes, 2) * ss;
-    const half2_t h3 = FP4_TO_F16X2(codes, 3) * ss;
-    return (half8_t){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
+// 16-byte chunk slot of chunk c in tile row r (8 chunks per row).
+NVFP4_DEV int chunk_slot(int r, int c) { return c ^ ((r ^ (r >> 1)) & 7); }
 
 // Two E4M3 bytes (byte 2*sel and 2*sel+1 of `w`) -> two f16 scales (exact).
 template <int kSel>
@@ -82,6 +77,24 @@ NVFP4_DEV half2_t scales2(uint32_t w)
 {
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kSel != 0);
 }
+
+// Decode 8 codes (one dword, element 2j in the low nibble of byte j) times
+// one f16 scale into a 16-byte f16 chunk.
+NVFP4_DEV u32x4 decode_chunk(uint32_t codes, _Float16 s)
+{
+    const half2_t ss = {s, s};
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss);
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss);
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss);
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss);
+    return r;
+}
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 NVFP4_DEV float silu_f(float g)
 {
@@ -95,15 +108,15 @@ gemm_kernel(GemmArgs p)
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 fragments per wave
-    constexpr int ROWS = BM + BN;
-    constexpr int CPT = (ROWS * 4 + NT - 1) / NT;  // 16-byte code chunks per thread per stage
-    constexpr int SPT = (ROWS + NT - 1) / NT;   // scale rows per thread per stage
+    constexpr int ROWS = BM + BN;               // tile rows: A rows, then W rows
+    constexpr int RPT = (ROWS + NT - 1) / NT;   // rows decoded per thread per stage
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 fragment");
     static_assert(MODE != kModeGateUp || FN % 2 == 0, "gate_up pairs gate and up fragments");
-    static_assert(NT % 4 == 0, "four threads per staged row");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds_codes[2][ROWS * kRowBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scales[2][ROWS * kRowScales];
+    // f16 operand tiles: A rows and W rows, 128 bytes per row per stage,
+    // written one stage ahead (ring of 2)
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kRowF16Bytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][BN * kRowF16Bytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -146,9 +159,8 @@ gemm_kernel(GemmArgs p)
     const int64_t kpb = K / 2, kpsb = K / 16;  // packed / scale bytes per row
     const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
     const uint8_t* wp = p.w_packed + (int64_t)e * w_rows * kpb;
-    const uint8_t* ws = p.w_scales + (int64_t)e * w_rows * kpsb;
+    const uint8_t* wsc = p.w_scales + (int64_t)e * w_rows * kpsb;
 
-    // ---- global source rows of this thread's staging chunks --------------
     auto a_row_of = [&](int r) -> int64_t {
         int64_t q = row_begin + r;
         if (q >= row_end)
@@ -159,59 +171,63 @@ gemm_kernel(GemmArgs p)
     };
     auto w_row_of = [&](int r) -> int64_t {
         if (MODE == kModeGateUp) {
+            // wave column group wn holds gate rows then the matching up rows
             const int wn = r / TN, rr = r % TN;
             const int64_t base = nt * (BN / 2) + wn * (TN / 2);
-            const int64_t i = rr < TN / 2 ? base + rr : base + (rr - TN / 2);
-            return rr < TN / 2 ? i : p.N + i;
+            return rr < TN / 2 ? base + rr : p.N + base + (rr - TN / 2);
         }
-        int64_t n = nt * BN + r;
+        const int64_t n = nt * BN + r;
         return n < p.N ? n : p.N - 1;
     };
 
-    const uint8_t* csrc[CPT];
-    int cdst[CPT];
-    const int cchunk = tid & 3;
+    // ---- rows this thread decodes from packed codes ----------------------
+    const uint8_t* csrc[RPT];
+    const uint8_t* ssrc[RPT];
+    int drow[RPT];
 #pragma unroll
-    for (int i = 0; i < CPT; i++) {
-        int row = (tid >> 2) + i * (NT / 4);
+    for (int i = 0; i < RPT; i++) {
+        int row = tid + i * NT;
         if (row >= ROWS)
-            row = ROWS - 1;  // surplus chunk of the last pass: reload a real row
-        if (row < BM)
-            csrc[i] = p.a_packed + a_row_of(row) * kpb + cchunk * 16;
-        else
-            csrc[i] = wp + w_row_of(row - BM) * kpb + cchunk * 16;
-        cdst[i] = row * kRowBytes + 16 * (cchunk ^ lds_swz(row));
+            row = ROWS - 1;  // surplus thread of the last pass: decodes the last row again
+        drow[i] = row;
+        if (row < BM) {
+            const int64_t ar = a_row_of(row);
+            csrc[i] = p.a_packed + ar * kpb;
+            ssrc[i] = p.a_scales + ar * kpsb;
+        } else {
+            const int64_t wr = w_row_of(row - BM);
+            csrc[i] = wp + wr * kpb;
+            ssrc[i] = wsc + wr * kpsb;
+        }
     }
-    const uint8_t* ssrc[SPT];
+    u32x4 creg[2][RPT][2];
+    uint32_t sreg[2][RPT];
+    const int64_t nstages = K / kBK;
+    auto load_stage = [&](int64_t st, int set) {
 #pragma unroll
-    for (int i = 0; i < SPT; i++) {
-        const int row = tid + i * NT;
-        const int rr = row < ROWS ? row : 0;
-        if (rr < BM)
-            ssrc[i] = p.a_scales + a_row_of(rr) * kpsb;
-        else
-            ssrc[i] = ws + w_row_of(rr - BM) * kpsb;
-    }
-
-    u32x4 creg[CPT];
-    u32x2 sreg[SPT];
-    auto load_stage = [&](int64_t s) {
-#pragma unroll
-        for (int i = 0; i < CPT; i++)
-            creg[i] = *(const u32x4*)(csrc[i] + s * kRowBytes);
-#pragma unroll
-        for (int i = 0; i < SPT; i++)
-            if (tid + i * NT < ROWS)
-                sreg[i] = *(const u32x2*)(ssrc[i] + s * kRowScales);
+        for (int i = 0; i < RPT; i++) {
+            const u32x4* c = (const u32x4*)(csrc[i] + st * kStageCodeBytes);
+            creg[set][i][0] = c[0];
+            creg[set][i][1] = c[1];
+            sreg[set][i] = *(const uint32_t*)(ssrc[i] + st * kStageScaleBytes);
+        }
     };
-    auto store_stage = [&](int buf) {
+    // decode part q (of 4: the 16-element block q) of the stage in register
+    // set `set` into tile buffer `buf`
+    auto decode_part = [&](int set, int buf, int part) {
 #pragma unroll
-        for (int i = 0; i < CPT; i++)
-            *(u32x4*)(&lds_codes[buf][cdst[i]]) = creg[i];
-#pragma unroll
-        for (int i = 0; i < SPT; i++)
-            if (tid + i * NT < ROWS)
-                *(u32x2*)(&lds_scales[buf][(tid + i * NT) * kRowScales]) = sreg[i];
+        for (int i = 0; i < RPT; i++) {
+            const uint32_t sw = sreg[set][i];
+            const half2_t s2 = part < 2 ? scales2<0>(sw) : scales2<1>(sw);
+            const _Float16 sc = (part & 1) ? s2.y : s2.x;
+            const u32x4 cv = creg[set][i][part >> 1];
+            const uint32_t c0 = (part & 1) ? cv.z : cv.x;
+            const uint32_t c1 = (part & 1) ? cv.w : cv.y;
+            const int r = drow[i];
+            uint8_t* rowp = r < BM ? &lds_a[buf][r * kRowF16Bytes] : &lds_w[buf][(r - BM) * kRowF16Bytes];
+            *(u32x4*)(rowp + 16 * chunk_slot(r, 2 * part)) = decode_chunk(c0, sc);
+            *(u32x4*)(rowp + 16 * chunk_slot(r, 2 * part + 1)) = decode_chunk(c1, sc);
+        }
     };
 
     float16_t acc[FM][FN];
@@ -222,91 +238,112 @@ gemm_kernel(GemmArgs p)
             acc[i][j] = (float16_t){};
 
     const int frow = lane & 31;  // fragment row of this lane
-    const int g = lane >> 5;     // K half of this lane
-    const int64_t nstages = K / kBK;
+    const int g = lane >> 5;     // which 8 of the 16 K-elements of an MFMA step
+    int aoff[FM], woff[FN];      // byte offset of this lane's fragment rows
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+        aoff[i] = (wave_m * TM + i * 32 + frow) * kRowF16Bytes;
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+        woff[j] = (wave_n * TN + j * 32 + frow) * kRowF16Bytes;
+    // the chunk slot depends on the row only through (row ^ row >> 1) & 7,
+    // the same for every fragment of this lane (rows differ by 32)
+    const int sw_a = ((wave_m * TM + frow) ^ ((wave_m * TM + frow) >> 1)) & 7;
+    const int sw_w = ((BM + wave_n * TN + frow) ^ ((BM + wave_n * TN + frow) >> 1)) & 7;
 
-    load_stage(0);
-    store_stage(0);
+    half8_t fa[2][FM], fw[2][FN];
+    auto read_frags = [&](const uint8_t* ta, const uint8_t* tw, int kk, int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            fa[slot][i] = *(const half8_t*)(ta + aoff[i] + 16 * ((2 * kk + g) ^ sw_a));
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            fw[slot][j] = *(const half8_t*)(tw + woff[j] + 16 * ((2 * kk + g) ^ sw_w));
+    };
+
+    // prologue: stage 0 decoded into buffers 0, packed stage 1 in registers
+    load_stage(0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+        decode_part(0, 0, q);
+    load_stage(nstages > 1 ? 1 : 0, 1);
     __syncthreads();
+    read_frags(lds_a[0], lds_w[0], 0, 0);
 
-    for (int64_t s = 0; s < nstages; s++) {
-        const int buf = (int)(s & 1);
-        if (s + 1 < nstages)
-            load_stage(s + 1);
-
-        const uint8_t* lc = lds_codes[buf];
-        const uint8_t* lsc = lds_scales[buf];
-        uint32_t sa[FM], sw[FN];
+    // one stage: MFMAs on buffers CUR (stage s) interleaved with decoding
+    // the packed stage s+1 (register set CUR ^ 1) into buffers CUR ^ 1.  CUR
+    // is a compile-time constant so both register sets stay in fixed
+    // registers.
+    auto stage = [&](int64_t s, auto cur_tag) {
+        constexpr int cur = decltype(cur_tag)::value, nxt = cur ^ 1;
+        // refill the register set stage s used (decoded last iteration);
+        // past the end reload the last stage (harmless, never decoded)
+        load_stage(s + 2 < nstages ? s + 2 : nstages - 1, cur);
+        // issue those loads first: they have the whole stage to land
+        __builtin_amdgcn_sched_group_barrier(0x020, 3 * RPT, 0);  // VMEM read
+        const uint8_t* ta = lds_a[cur];
+        const uint8_t* tw = lds_w[cur];
 #pragma unroll
-        for (int i = 0; i < FM; i++) {
-            const int row = wave_m * TM + i * 32 + frow;
-            sa[i] = *(const uint32_t*)(lsc + row * kRowScales + 4 * g);
-        }
+        for (int kk = 0; kk < 4; kk++) {
+            const int sl = kk & 1;
+            // fragments of the next k-step first, fenced so the scheduler
+            // cannot sink them next to their use
+            if (kk < 3)
+                read_frags(ta, tw, kk + 1, sl ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int row = BM + wave_n * TN + j * 32 + frow;
-            sw[j] = *(const uint32_t*)(lsc + row * kRowScales + 4 * g);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            u32x4 ca[FM], cw[FN];
-            half2_t sca[FM], scw[FN];
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                const int row = wave_m * TM + i * 32 + frow;
-                ca[i] = *(const u32x4*)(lc + row * kRowBytes + 16 * ((2 * g + t) ^ lds_swz(row)));
-                sca[i] = t == 0 ? scales2<0>(sa[i]) : scales2<1>(sa[i]);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; j++) {
-                const int row = BM + wave_n * TN + j * 32 + frow;
-                cw[j] = *(const u32x4*)(lc + row * kRowBytes + 16 * ((2 * g + t) ^ lds_swz(row)));
-                scw[j] = t == 0 ? scales2<0>(sw[j]) : scales2<1>(sw[j]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++) {
-                half8_t fa[FM], fw[FN];
-#pragma unroll
-                for (int i = 0; i < FM; i++)
-                    fa[i] = decode8(ca[i][kk], kk < 2 ? sca[i].x : sca[i].y);
+            for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++)
-                    fw[j] = decode8(cw[j][kk], kk < 2 ? scw[j].x : scw[j].y);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fw[sl][j], acc[i][j], 0, 0, 0);
+            // decode 1/4 of the next stage (the last iteration decodes stale
+            // registers into a buffer nobody reads again)
+            decode_part(nxt, nxt, kk);
+            // interleave the decode VALU work and its stores between MFMAs
 #pragma unroll
-                for (int i = 0; i < FM; i++)
-#pragma unroll
-                    for (int j = 0; j < FN; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fw[j], acc[i][j], 0, 0, 0);
+            for (int m = 0; m < FM * FN; m++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+                if (m % 4 == 3)
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (s + 1 < nstages)
-            store_stage(buf ^ 1);
         __syncthreads();
+        read_frags(lds_a[nxt], lds_w[nxt], 0, 0);
+    };
+    int64_t s = 0;
+    for (; s + 1 < nstages; s += 2) {
+        stage(s, IntC<0>{});
+        stage(s + 1, IntC<1>{});
     }
+    if (s < nstages)
+        stage(s, IntC<0>{});
 
     // ---- epilogue --------------------------------------------------------
-    const float ga = *p.a_global;
-    const float gw = p.w_global[e];
-    const float gscale = ga * gw;
+    const float gscale = *p.a_global * p.w_global[e];
     const int ncol = lane & 31;
     const int rsub = 4 * (lane >> 5);
+    const int64_t wrow0 = row_begin + wave_m * TM;  // first output row of this wave
 
     if (MODE == kModeGateUp) {
-        uint16_t* h = (uint16_t*)p.out;
+        const int64_t col0 = nt * (BN / 2) + wave_n * (TN / 2) + ncol;
+        uint16_t* h = (uint16_t*)p.out + wrow0 * p.N + col0;
+        const int ld = (int)p.N;
+        const int rows_left = (int)(row_end - wrow0);
         uint32_t hmax = 0;
 #pragma unroll
         for (int i = 0; i < FM; i++) {
 #pragma unroll
-            for (int j = 0; j < FN / 2; j++) {
-                const int64_t col = nt * (BN / 2) + wave_n * (TN / 2) + j * 32 + ncol;
+            for (int r = 0; r < 16; r++) {
+                const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
+                if (rr < rows_left) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int64_t q = row_begin + wave_m * TM + i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
-                    const float gg = acc[i][j][r] * gscale;
-                    const float uu = acc[i][j + FN / 2][r] * gscale;
-                    const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
-                    if (q < row_end) {
-                        h[q * p.N + col] = hb;
+                    for (int j = 0; j < FN / 2; j++) {
+                        const float gg = acc[i][j][r] * gscale;
+                        const float uu = acc[i][j + FN / 2][r] * gscale;
+                        const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+                        h[rr * ld + j * 32] = hb;
                         const uint32_t mag = hb & 0x7FFFu;
                         hmax = hmax > mag ? hmax : mag;
                     }
@@ -317,24 +354,316 @@ gemm_kernel(GemmArgs p)
         if (lane == 0 && hmax != 0)
             atomicMax(p.h_amax, hmax << 16);
     } else {
+        const int64_t col0 = nt * BN + wave_n * TN + ncol;
+        const int ld = (int)p.N;
+        const int rows_left = (int)(row_end - wrow0);
+        const bool bf16_out = MODE == kModeDense && p.out_bf16;
+        float* of = (float*)p.out + wrow0 * p.N + col0;
+        uint16_t* ob = (uint16_t*)p.out + wrow0 * p.N + col0;
 #pragma unroll
         for (int i = 0; i < FM; i++) {
 #pragma unroll
-            for (int j = 0; j < FN; j++) {
-                const int64_t col = nt * BN + wave_n * TN + j * 32 + ncol;
+            for (int r = 0; r < 16; r++) {
+                const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
+                if (rr < rows_left) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int64_t q = row_begin + wave_m * TM + i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
-                    if (q < row_end && col < p.N) {
-                        const float v = acc[i][j][r] * gscale;
-                        if (MODE == kModeDense && p.out_bf16)
-                            ((uint16_t*)p.out)[q * p.N + col] = f32_to_bf16(v);
-                        else
-                            ((float*)p.out)[q * p.N + col] = v;
+                    for (int j = 0; j < FN; j++) {
+                        if (col0 + j * 32 < p.N) {
+                            const float v = acc[i][j][r] * gscale;
+                            if (bf16_out)
+                                ob[rr * ld + j * 32] = f32_to_bf16(v);
+                            else
+                                of[rr * ld + j * 32] = v;
+                        }
                     }
                 }
             }
         }
+    }
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// Weight-streaming W4A4 GEMM for few A rows (decode batches: 16 A rows per
+// tile).
+//
+// With few A rows the GEMM is bound by reading the 4-bit weights, so each
+// weight byte is read from HBM once, in whole 128-byte lines, and decoded
+// once.  A workgroup of 4 waves owns 128 W rows (32 per wave, as two 16-row
+// fragments of v_mfma_f32_16x16x32_f16) and walks K in stages of 256
+// elements.  Each thread loads 16-byte pieces so that 8 consecutive lanes
+// cover one row's 128 bytes of a stage; the pieces sit in registers two
+// stages ahead, then go to a swizzled LDS tile from which every lane reads
+// the codes of its own row.  The few A rows are decoded once per workgroup
+// into an f16 LDS tile.  Inside a stage the K order is permuted the same way
+// for both operands: k-step kk = 4 q + d (q < 2, d < 4) gives lane group
+// kg = lane / 16 the stage elements [128 q + 32 kg + 8 d, +8).  When the
+// tiles alone cannot fill the chip, K is split over several workgroups
+// (dense mode only) and a second kernel adds their partial sums in a fixed
+// order.
+// ---------------------------------------------------------------------------
+constexpr int kSkBK = 256;               // K elements per stage
+constexpr int kSkRowF16 = kSkBK * 2;     // f16 A-tile bytes per row per stage
+constexpr int kSkBM = 16;                // A rows per tile
+constexpr int kSkBN = 128;               // W rows per workgroup
+constexpr int kSkThreads = 256;
+
+// 16-byte slot of piece c (of 8) in W tile row r: rows r and r + 1 fall in
+// different halves of the banks, and the 8 even (odd) rows of a 16-row
+// fragment get 8 different slots, so a 16-lane read phase is conflict free.
+NVFP4_DEV int sk_wslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+// 16-byte slot of f16 chunk c (of 32) in A tile row r
+NVFP4_DEV int sk_aslot(int r, int c) { return c ^ (r & 15); }
+
+template <int MODE>
+__global__ void __launch_bounds__(kSkThreads)
+gemm_stream_kernel(GemmArgs p)
+{
+    constexpr int BM = kSkBM, BN = kSkBN;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][BN * 128];        // codes, 2 x 16 KiB
+    __shared__ __attribute__((aligned(16))) uint8_t lds_ws[2][BN * 16];        // scales, 2 x 2 KiB
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kSkRowF16];  // f16 A, 2 x 8 KiB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 15, kg = lane >> 4;
+
+    // ---- tile assignment: the A tile index varies fastest, so the tiles
+    // that share W rows run together on one XCD and share its L2 ----------
+    const int64_t nblocks = (int64_t)gridDim.x;
+    int64_t bid = blockIdx.x;
+    if ((nblocks & 7) == 0)
+        bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    const int64_t mt = bid % p.m_tiles;
+    const int64_t rest = bid / p.m_tiles;
+    const int ks = (int)(rest % p.ksplit);
+    const int64_t nt = rest / p.ksplit;
+    if (nt >= p.n_tiles)
+        return;
+
+    int e = 0;
+    int64_t row_begin, row_end;
+    if (MODE == kModeDense) {
+        row_begin = mt * BM;
+        row_end = row_begin + BM < p.M ? row_begin + BM : p.M;
+    } else {
+        if (mt >= p.tile_off[p.experts])
+            return;
+        int lo = 0, hi = p.experts - 1;  // largest e with tile_off[e] <= mt
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.tile_off[mid] <= mt)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        e = lo;
+        row_begin = p.offsets[e] + (mt - p.tile_off[e]) * BM;
+        const int64_t eend = p.offsets[e + 1];
+        row_end = row_begin + BM < eend ? row_begin + BM : eend;
+    }
+
+    const int64_t K = p.K;
+    const int64_t kpb = K / 2, kpsb = K / 16;
+    const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
+    const uint8_t* wp = p.w_packed + (int64_t)e * w_rows * kpb;
+    const uint8_t* wsc = p.w_scales + (int64_t)e * w_rows * kpsb;
+
+    // stages [st0, st0 + nstages) of this split
+    const int64_t nst_all = K / kSkBK;
+    const int64_t st0 = nst_all * ks / p.ksplit;
+    const int64_t nstages = nst_all * (ks + 1) / p.ksplit - st0;
+
+    // tile row r -> W row.  Wave w's fragment f is tile rows 32 w + 16 f +
+    // [0, 16); in gate_up mode fragment 0 holds gate rows and fragment 1 the
+    // matching up rows.
+    auto w_row_of = [&](int r) -> int64_t {
+        if (MODE == kModeGateUp) {
+            const int64_t c = nt * (BN / 2) + 16 * (r >> 5) + (r & 15);
+            return ((r >> 4) & 1) == 0 ? c : p.N + c;
+        }
+        const int64_t n = nt * BN + r;
+        return n < p.N ? n : p.N - 1;  // ragged last tile: reread a valid row, never stored
+    };
+
+    // ---- this thread's loads: W code pieces j (tile row 32 j + tid / 8,
+    // piece tid % 8), then either a W scale row (threads < 128) or an A
+    // piece (threads >= 128: A row (tid - 128) / 8, piece tid % 8) ---------
+    const int pc = tid & 7;
+    const uint8_t* wsrc[4];
+    int wdst[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int r = 32 * j + (tid >> 3);
+        wsrc[j] = wp + w_row_of(r) * kpb + st0 * (kSkBK / 2) + 16 * pc;
+        wdst[j] = r * 128 + 16 * sk_wslot(r, pc);
+    }
+    const bool loads_scales = tid < 128;
+    const int arow = (tid >> 3) & 15;
+    int64_t aq = row_begin + arow;
+    if (aq >= row_end)
+        aq = row_begin;  // padding rows repeat a valid row; never stored
+    const int64_t ar = MODE == kModeGateUp ? p.perm[aq] / p.topk : aq;
+    const uint8_t* xsrc = loads_scales ? wsc + w_row_of(tid) * kpsb + st0 * (kSkBK / 16)
+                                       : p.a_packed + ar * kpb + st0 * (kSkBK / 2) + 16 * pc;
+    const uint8_t* ysrc = p.a_scales + ar * kpsb + st0 * (kSkBK / 16) + 2 * pc;
+
+    u32x4 wreg[3][4];
+    u32x4 xreg[3];
+    uint32_t yreg[3];
+    auto load_stage = [&](int64_t st, int set) {
+        const int64_t xo = loads_scales ? st * (kSkBK / 16) : st * (kSkBK / 2);
+        xreg[set] = *(const u32x4*)(xsrc + xo);
+        yreg[set] = *(const uint16_t*)(ysrc + st * (kSkBK / 16));
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            wreg[set][j] = *(const u32x4*)(wsrc[j] + st * (kSkBK / 2));
+    };
+    // registers of a stage -> LDS buffer b (A decoded to f16 on the way)
+    auto store_stage = [&](int set, int b) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            *(u32x4*)(&lds_w[b][wdst[j]]) = wreg[set][j];
+        if (loads_scales) {
+            *(u32x4*)(&lds_ws[b][16 * tid]) = xreg[set];
+        } else {
+            const half2_t s2 = scales2<0>(yreg[set]);
+            uint8_t* rowp = &lds_a[b][arow * kSkRowF16];
+            const u32x4 cv = xreg[set];
+            *(u32x4*)(rowp + 16 * sk_aslot(arow, 4 * pc + 0)) = decode_chunk(cv.x, s2.x);
+            *(u32x4*)(rowp + 16 * sk_aslot(arow, 4 * pc + 1)) = decode_chunk(cv.y, s2.x);
+            *(u32x4*)(rowp + 16 * sk_aslot(arow, 4 * pc + 2)) = decode_chunk(cv.z, s2.y);
+            *(u32x4*)(rowp + 16 * sk_aslot(arow, 4 * pc + 3)) = decode_chunk(cv.w, s2.y);
+        }
+    };
+
+    typedef float float4_t __attribute__((ext_vector_type(4)));
+    float4_t acc[2] = {(float4_t){}, (float4_t){}};
+
+    auto compute = [&](int b) {
+        const uint8_t* ta = lds_a[b] + fr * kSkRowF16;
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            u32x4 piece[2];
+            half2_t s2[2];
+#pragma unroll
+            for (int f = 0; f < 2; f++) {
+                const int r = 32 * wave + 16 * f + fr;
+                piece[f] = *(const u32x4*)(&lds_w[b][r * 128 + 16 * sk_wslot(r, 4 * q + kg)]);
+                // blocks 8 q + 2 kg + {0, 1} of the stage
+                s2[f] = scales2<0>(*(const uint16_t*)(&lds_ws[b][r * 16 + 8 * q + 2 * kg]));
+            }
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                const half8_t fa = *(const half8_t*)(ta + 16 * sk_aslot(fr, 16 * q + 4 * kg + d));
+#pragma unroll
+                for (int f = 0; f < 2; f++) {
+                    const u32x4 pv = piece[f];
+                    const uint32_t codes = d == 0 ? pv.x : d == 1 ? pv.y : d == 2 ? pv.z : pv.w;
+                    const u32x4 dv = decode_chunk(codes, d < 2 ? s2[f].x : s2[f].y);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, __builtin_bit_cast(half8_t, dv),
+                                                                    acc[f], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // ---- pipeline: registers hold stages s+2 and s+3 in flight while stage
+    // s+1 goes to LDS and stage s is computed; one barrier per stage -------
+    const int64_t last = nstages - 1;
+    load_stage(0, 0);
+    load_stage(last < 1 ? last : 1, 1);
+    load_stage(last < 2 ? last : 2, 2);
+    store_stage(0, 0);
+    __syncthreads();
+    auto iter = [&](int64_t s, auto set_tag) {
+        constexpr int cur = decltype(set_tag)::value;  // register set of stage s (and s+3)
+        constexpr int nxt = (cur + 1) % 3;              // register set of stage s+1
+        store_stage(nxt, (int)((s + 1) & 1));
+        load_stage(s + 3 <= last ? s + 3 : last, cur);
+        compute((int)(s & 1));
+        __syncthreads();
+    };
+    int64_t s = 0;
+    for (; s + 3 <= nstages; s += 3) {
+        iter(s, IntC<0>{});
+        iter(s + 1, IntC<1>{});
+        iter(s + 2, IntC<2>{});
+    }
+    if (s < nstages)
+        iter(s, IntC<0>{});
+    if (s + 1 < nstages)
+        iter(s + 1, IntC<1>{});
+
+    // ---- epilogue: lane holds output rows 4 kg + i, column fr of each
+    // fragment ------------------------------------------------------------
+    const float gscale = *p.a_global * p.w_global[e];
+    const int rows_left = (int)(row_end - row_begin);
+    if (MODE == kModeGateUp) {
+        const int64_t col = nt * (BN / 2) + 16 * wave + fr;
+        uint16_t* h = (uint16_t*)p.out + row_begin * p.N + col;
+        uint32_t hmax = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = 4 * kg + i;
+            if (m < rows_left) {
+                const float gg = acc[0][i] * gscale;
+                const float uu = acc[1][i] * gscale;
+                const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+                h[(int64_t)m * p.N] = hb;
+                const uint32_t mag = hb & 0x7FFFu;
+                hmax = hmax > mag ? hmax : mag;
+            }
+        }
+        hmax = wave_max_u32(hmax);
+        if (lane == 0 && hmax != 0)
+            atomicMax(p.h_amax, hmax << 16);
+    } else {
+        const bool split = MODE == kModeDense && p.ksplit > 1;
+        const bool bf16_out = MODE == kModeDense && p.out_bf16;
+        float* part = split ? p.partial + (int64_t)ks * p.M * p.N : nullptr;
+#pragma unroll
+        for (int f = 0; f < 2; f++) {
+            const int64_t col = nt * BN + 32 * wave + 16 * f + fr;
+            if (col < p.N) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = 4 * kg + i;
+                    if (m < rows_left) {
+                        const int64_t o = (row_begin + m) * p.N + col;
+                        if (split)
+                            part[o] = acc[f][i];
+                        else if (bf16_out)
+                            ((uint16_t*)p.out)[o] = f32_to_bf16(acc[f][i] * gscale);
+                        else
+                            ((float*)p.out)[o] = acc[f][i] * gscale;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Sum the K-split partials in split order, scale by G_A * G_W and
+// store fp32 or bf16.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t count,
+                     const float* a_global, const float* w_global, void* out, int out_bf16)
+{
+    const float gscale = *a_global * *w_global;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float acc = partial[i];
+        for (int s = 1; s < ksplit; s++)
+            acc += partial[(int64_t)s * count + i];
+        const float v = acc * gscale;
+        if (out_bf16)
+            ((uint16_t*)out)[i] = f32_to_bf16(v);
+        else
+            ((float*)out)[i] = v;
     }
 }
 

@@ -116,12 +116,77 @@ nvfp4_status launch_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     return launch_status();
 }
 
+// The weight-streaming kernel serves A operands of at most 32 rows per
+// expert (on average; tiles of 16 rows) when K is a multiple of its
+// 256-element stage.
+bool use_stream_gemm(int64_t rows_avg, int64_t K) { return rows_avg <= 2 * kSkBM && K > 0 && K % kSkBK == 0; }
+
+// K split of the dense weight-streaming GEMM: at most one workgroup per
+// resident slot (3 per CU on 256 CUs), at least four stages per split,
+// partials <= 32 MiB.
+int gemm_ksplit(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || !use_stream_gemm(M, K))
+        return 1;
+    const int64_t base = ceil_div(M, kSkBM) * ceil_div(N, kSkBN);
+    int64_t s = 768 / base;
+    s = std::min<int64_t>(s, K / kSkBK / 4);
+    s = std::min<int64_t>(s, ((int64_t)32 << 20) / (M * N * 4));
+    return (int)std::max<int64_t>(1, s);
+}
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int s = gemm_ksplit(M, N, K);
+    return s > 1 ? align256((size_t)s * M * N * sizeof(float)) : 0;
+}
+
+template <int MODE>
+nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
+{
+    p.m_tiles = m_tiles_ub;
+    int64_t blocks = m_tiles_ub * p.n_tiles * p.ksplit;
+    if (blocks == 0)
+        return NVFP4_OK;
+    blocks = ceil_div(blocks, 8) * 8;
+    if (blocks > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    gemm_stream_kernel<MODE><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    nvfp4_status s = launch_status();
+    if (s != NVFP4_OK || p.ksplit <= 1)
+        return s;
+    const int64_t count = p.M * p.N;
+    const unsigned rb = (unsigned)std::min<int64_t>(2048, ceil_div(count, 256));
+    splitk_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, count, p.a_global, p.w_global, p.out,
+                                             p.out_bf16);
+    return launch_status();
+}
+
 // Tile configurations: (BM, BN, waves).  Chosen by the rows an expert (or
 // the dense A) holds on average.
 template <int MODE>
 nvfp4_status dispatch_gemm(GemmArgs p, int64_t rows_avg, int64_t total_rows, int experts,
                            int32_t* tile_off_ws, hipStream_t st)
 {
+    if (p.ksplit < 1)
+        p.ksplit = 1;
+    if (use_stream_gemm(rows_avg, p.K)) {
+        p.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? kSkBN / 2 : kSkBN);
+        int64_t m_ub;
+        if (MODE == kModeDense) {
+            m_ub = ceil_div(total_rows, kSkBM);
+        } else {
+            p.ksplit = 1;
+            tile_offsets_kernel<<<1, 1024, 0, st>>>(p.offsets, experts, kSkBM, tile_off_ws);
+            nvfp4_status s = launch_status();
+            if (s != NVFP4_OK)
+                return s;
+            p.tile_off = tile_off_ws;
+            m_ub = ceil_div(total_rows, kSkBM) + experts;
+        }
+        return launch_stream_gemm<MODE>(p, m_ub, st);
+    }
+    p.ksplit = 1;
     int bm;
     if (rows_avg >= 256)
         bm = 256;
@@ -269,7 +334,10 @@ size_t nvfp4_workspace_size(int op, int64_t T, int32_t k, int32_t E, int64_t H, 
         return align256((size_t)(batch * blocks)) + 2 * align256(sizeof(int) * kRemapParts * batch);
     }
     case NVFP4_OP_GEMM:
-        return 0;
+        // T = M (A rows), H = K, I = N (W rows)
+        if (T <= 0 || H <= 0 || I <= 0)
+            return 0;
+        return gemm_ws_bytes(T, I, H);
     case NVFP4_OP_MOE:
         if (T < 0 || k < 1 || E < 1)
             return 0;
@@ -393,7 +461,7 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0, int64
 }
 
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, nvfp4_dtype dtype,
-                        void* stream)
+                        void* ws, size_t ws_bytes, void* stream)
 {
     nvfp4_status s = check_tensor(A);
     if (s == NVFP4_OK)
@@ -423,6 +491,16 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
     p.experts = 1;
     p.out = C;
     p.out_bf16 = dtype == NVFP4_BF16;
+    p.ksplit = 1;
+    const int ksplit = gemm_ksplit(p.M, p.N, p.K);
+    if (ksplit > 1 && ws) {
+        if (!aligned(ws, 256))
+            return NVFP4_ERR_INVALID_ARG;
+        if (ws_bytes < gemm_ws_bytes(p.M, p.N, p.K))
+            return NVFP4_ERR_WORKSPACE;
+        p.ksplit = ksplit;
+        p.partial = (float*)ws;
+    }
     return dispatch_gemm<kModeDense>(p, A->rows, A->rows, 1, nullptr, S(stream));
 }
 
@@ -566,7 +644,7 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         return s;
     if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    if (H % kBK != 0 || I % kBK != 0)
+    if (H % kBK != 0 || I % 128 != 0)
         return NVFP4_ERR_UNSUPPORTED;
     if (T == 0)
         return NVFP4_OK;

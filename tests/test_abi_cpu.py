@@ -57,6 +57,13 @@ def test_workspace_sizes(lib):
     from precision_moe_gemm_amd import _lib
     assert nv.nvfp4_workspace_size(_lib.OP_QUANTIZE) == 4096
     assert nv.nvfp4_workspace_size(_lib.OP_GEMM) == 0
+    # few-row GEMMs with a long K split it: partial sums M x N fp32 per split
+    sk = nv.nvfp4_workspace_size(_lib.OP_GEMM, 1, 0, 0, 17408, 5120)
+    assert sk >= 2 * 5120 * 4 and sk % 256 == 0
+    assert nv.nvfp4_workspace_size(_lib.OP_GEMM, 32, 0, 0, 17408, 5120) <= 32 << 20
+    # many rows (MFMA-bound tiles) or a K that is not a multiple of 256: no split
+    assert nv.nvfp4_workspace_size(_lib.OP_GEMM, 8192, 0, 0, 5120, 34816) == 0
+    assert nv.nvfp4_workspace_size(_lib.OP_GEMM, 1, 0, 0, 192, 5120) == 0
     a = nv.nvfp4_workspace_size(_lib.OP_MOE, 4096, 10, 512, 4096, 1024)
     b = nv.nvfp4_workspace_size(_lib.OP_MOE, 4096, 10, 512, 4096, 2048)
     assert 0 < a < b
@@ -79,12 +86,17 @@ def test_host_validation_fails_before_launch(lib):
     # bad dtype
     T4 = _lib.NVFP4TensorC(16, 16, 16, 4, 32, 1)
     assert lib.nvfp4_dequantize(ctypes.byref(T4), ctypes.c_void_p(16), 7, None) == _lib.INVALID_ARG
-    # GEMM with K not a multiple of 128 -> unsupported; mismatched K -> shape
+    # GEMM with K not a multiple of 64 -> unsupported; mismatched K -> shape
     A = _lib.NVFP4TensorC(16, 16, 16, 4, 80, 1)
     W = _lib.NVFP4TensorC(16, 16, 16, 8, 80, 1)
-    assert lib.nvfp4_gemm(ctypes.byref(A), ctypes.byref(W), ctypes.c_void_p(16), 0, None) == _lib.UNSUPPORTED
+    assert lib.nvfp4_gemm(ctypes.byref(A), ctypes.byref(W), ctypes.c_void_p(16), 0, None, 0, None) == _lib.UNSUPPORTED
+    # a workspace smaller than the split needs -> workspace error
+    A1 = _lib.NVFP4TensorC(16, 16, 16, 1, 4096, 1)
+    W1 = _lib.NVFP4TensorC(16, 16, 16, 256, 4096, 1)
+    assert lib.nvfp4_gemm(ctypes.byref(A1), ctypes.byref(W1), ctypes.c_void_p(16), 0, ctypes.c_void_p(256), 64,
+                          None) == _lib.WORKSPACE
     W2 = _lib.NVFP4TensorC(16, 16, 16, 8, 96, 1)
-    assert lib.nvfp4_gemm(ctypes.byref(A), ctypes.byref(W2), ctypes.c_void_p(16), 0, None) == _lib.SHAPE
+    assert lib.nvfp4_gemm(ctypes.byref(A), ctypes.byref(W2), ctypes.c_void_p(16), 0, None, 0, None) == _lib.SHAPE
     # remap: cols % 32
     O = _lib.NVFP4TensorC(16, 16, 16, 4, 48, 1)
     assert lib.mxfp4_to_nvfp4(ctypes.c_void_p(16), ctypes.c_void_p(16), 4, 48, 1, ctypes.byref(O),

@@ -49,6 +49,51 @@ def test_random_shapes(orc, M, N, K):
     assert rel_err(C, R) <= GEMM_TOL
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 300, 256), (5, 256, 768), (17, 1000, 4096), (32, 520, 1024),
+                                   (1, 5120, 17408), (32, 264, 2560), (2, 34816, 512)])
+def test_weight_streaming_shapes(orc, M, N, K):
+    """Few-row shapes (<= 32 rows, K % 256 == 0) take the weight-streaming
+    kernel, with K split over workgroups when the tiles alone are few."""
+    x = synth.normal_bf16((M, K), 1.0, (310, M, K))
+    w = synth.normal_bf16((N, K), 0.02, (311, N, K))
+    step(f"gemm weight streaming M={M} N={N} K={K}")
+    A, W = _q(x), _q(w)
+    C = nv.nvfp4_gemm(A, W)
+    Cb = nv.nvfp4_gemm(A, W, torch.bfloat16)
+    torch.cuda.synchronize()
+    Ao, Wo = to_oracle(A), to_oracle(W)
+    if N * K <= 1 << 22:
+        R = orc.gemm(Ao, Wo)
+        got, gotb = C.cpu().numpy(), Cb.float().cpu().numpy()
+    else:
+        cols = np.unique(np.r_[np.random.default_rng(N).choice(N, 64, replace=False), 0, N - 1])
+        R = orc.gemm_rows(Ao, orc.NVFP4(u8(W.packed)[0][cols], u8(W.scales)[0][cols], W.global_.item()))
+        got, gotb = C.cpu().numpy()[:, cols], Cb.float().cpu().numpy()[:, cols]
+    err = rel_err(got, R)
+    print(f"streaming M={M} N={N} K={K} rel err {err:.3e}")
+    assert err <= GEMM_TOL
+    assert rel_err(gotb, R) <= GEMM_TOL + BF16_HALF_ULP
+
+
+def test_split_k_matches_unsplit_and_is_reproducible():
+    M, N, K = 3, 1024, 8192
+    A = _q(synth.normal_bf16((M, K), 1.0, (320, 0)))
+    W = _q(synth.normal_bf16((N, K), 0.02, (321, 0)))
+    nbytes = nv.nvfp4_workspace_size(2, M, 0, 0, K, N)
+    assert nbytes > 0
+    step("gemm split-K vs unsplit")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    a = nv.nvfp4_gemm(A, W, ws=ws)
+    b = nv.nvfp4_gemm(A, W, ws=ws)
+    c = nv.nvfp4_gemm(A, W, ws=torch.empty(0, dtype=torch.uint8, device=DEV))  # size 0: unsplit
+    assert torch.equal(a, b)
+    ref = c.double()
+    assert ((a.double() - ref).abs().max() / ref.abs().max()).item() <= GEMM_TOL
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.nvfp4_gemm(A, W, ws=ws[: nbytes // 2])
+    assert ei.value.status == 4
+
+
 def test_integer_special_case_is_exact(orc):
     rng = np.random.default_rng(4)
     M, N, K = 64, 512, 1024
