@@ -53,17 +53,20 @@ struct GemmArgs {
     int64_t N;                // output columns (dense/down: rows of W; gate_up: I)
     int64_t n_tiles;          // output column tiles
     int64_t m_tiles;          // dense: m tiles; grouped: upper bound
-    // grouped: list positions of expert e are [offsets[e], offsets[e+1])
-    const int32_t* offsets;
+    // grouped: tile i of expert e covers list positions
+    // [row_base[e] + i BM, min(+BM, row_lim[e])), i < tile_off[e+1] - tile_off[e]
     const int32_t* tile_off;  // [experts+1] prefix of m tiles per expert
+    const int32_t* row_base;  // [experts]
+    const int32_t* row_lim;   // [experts]
     const int32_t* perm;      // gate_up: list position -> t*k + j
     int32_t topk;
     int32_t experts;
     void* out;                // dense: C; gate_up: h bf16 [T*k, I]; down: y fp32
     int out_bf16;             // dense only
     uint32_t* h_amax;         // gate_up only
-    // weight-streaming kernel, dense mode: K split over `ksplit` workgroups
-    // whose raw fp32 sums go to partial[ksplit][M][N] (ksplit > 1 only)
+    // weight-streaming kernel (dense and down modes): K split over `ksplit`
+    // workgroups whose scaled fp32 sums go to partial[ksplit][M][N]
+    // (ksplit > 1 only; M = rows of the output)
     int32_t ksplit;
     float* partial;
 };
@@ -89,6 +92,19 @@ NVFP4_DEV u32x4 decode_chunk(uint32_t codes, _Float16 s)
     r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss);
     r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss);
     return r;
+}
+
+// Work item of this workgroup, or -1.  Workgroups are dispatched to the 8
+// XCDs round-robin by id, so XCD (id % 8) takes a contiguous eighth of the
+// `items` real work items (neighbouring tiles share operands through that
+// XCD's L2).  The grid may hold more workgroups than items (grouped launches
+// size it by an upper bound): the surplus exits here, on every XCD alike.
+NVFP4_DEV int64_t xcd_item(int64_t items)
+{
+    const int64_t per = (items + 7) >> 3;
+    const int64_t j = (int64_t)(blockIdx.x >> 3);
+    const int64_t it = (int64_t)(blockIdx.x & 7) * per + j;
+    return (j < per && it < items) ? it : -1;
 }
 
 template <int V>
@@ -124,10 +140,10 @@ gemm_kernel(GemmArgs p)
 
     // ---- tile assignment (XCD-aware: consecutive ids go round-robin over 8
     // XCDs, so give each XCD a contiguous range of logical tiles) ----------
-    const int64_t nblocks = (int64_t)gridDim.x;
-    int64_t bid = blockIdx.x;
-    if ((nblocks & 7) == 0)
-        bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    const int64_t m_act = MODE == kModeDense ? p.m_tiles : p.tile_off[p.experts];
+    const int64_t bid = xcd_item(m_act * p.n_tiles);
+    if (bid < 0)
+        return;
     const int64_t mt = bid / p.n_tiles;
     const int64_t nt = bid - mt * p.n_tiles;
 
@@ -150,8 +166,8 @@ gemm_kernel(GemmArgs p)
                 hi = mid - 1;
         }
         e = lo;
-        row_begin = p.offsets[e] + (mt - p.tile_off[e]) * BM;
-        const int64_t eend = p.offsets[e + 1];
+        row_begin = p.row_base[e] + (mt - p.tile_off[e]) * BM;
+        const int64_t eend = p.row_lim[e];
         row_end = row_begin + BM < eend ? row_begin + BM : eend;
     }
 
@@ -433,16 +449,14 @@ gemm_stream_kernel(GemmArgs p)
 
     // ---- tile assignment: the A tile index varies fastest, so the tiles
     // that share W rows run together on one XCD and share its L2 ----------
-    const int64_t nblocks = (int64_t)gridDim.x;
-    int64_t bid = blockIdx.x;
-    if ((nblocks & 7) == 0)
-        bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
-    const int64_t mt = bid % p.m_tiles;
-    const int64_t rest = bid / p.m_tiles;
+    const int64_t m_act = MODE == kModeDense ? p.m_tiles : p.tile_off[p.experts];
+    const int64_t bid = xcd_item(m_act * p.n_tiles * p.ksplit);
+    if (bid < 0)
+        return;
+    const int64_t mt = bid % m_act;
+    const int64_t rest = bid / m_act;
     const int ks = (int)(rest % p.ksplit);
     const int64_t nt = rest / p.ksplit;
-    if (nt >= p.n_tiles)
-        return;
 
     int e = 0;
     int64_t row_begin, row_end;
@@ -461,8 +475,8 @@ gemm_stream_kernel(GemmArgs p)
                 hi = mid - 1;
         }
         e = lo;
-        row_begin = p.offsets[e] + (mt - p.tile_off[e]) * BM;
-        const int64_t eend = p.offsets[e + 1];
+        row_begin = p.row_base[e] + (mt - p.tile_off[e]) * BM;
+        const int64_t eend = p.row_lim[e];
         row_end = row_begin + BM < eend ? row_begin + BM : eend;
     }
 
@@ -622,7 +636,8 @@ gemm_stream_kernel(GemmArgs p)
         if (lane == 0 && hmax != 0)
             atomicMax(p.h_amax, hmax << 16);
     } else {
-        const bool split = MODE == kModeDense && p.ksplit > 1;
+        // K split: split ks writes its scaled partial sums to plane ks
+        const bool split = p.ksplit > 1;
         const bool bf16_out = MODE == kModeDense && p.out_bf16;
         float* part = split ? p.partial + (int64_t)ks * p.M * p.N : nullptr;
 #pragma unroll
@@ -635,7 +650,7 @@ gemm_stream_kernel(GemmArgs p)
                     if (m < rows_left) {
                         const int64_t o = (row_begin + m) * p.N + col;
                         if (split)
-                            part[o] = acc[f][i];
+                            part[o] = acc[f][i] * gscale;
                         else if (bf16_out)
                             ((uint16_t*)p.out)[o] = f32_to_bf16(acc[f][i] * gscale);
                         else
@@ -647,19 +662,15 @@ gemm_stream_kernel(GemmArgs p)
     }
 }
 
-// Sum the K-split partials in split order, scale by G_A * G_W and
-// store fp32 or bf16.
+// Sum the scaled K-split partials in split order and store fp32 or bf16.
 __global__ void __launch_bounds__(256)
-splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t count,
-                     const float* a_global, const float* w_global, void* out, int out_bf16)
+splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t count, void* out, int out_bf16)
 {
-    const float gscale = *a_global * *w_global;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x) {
-        float acc = partial[i];
+        float v = partial[i];
         for (int s = 1; s < ksplit; s++)
-            acc += partial[(int64_t)s * count + i];
-        const float v = acc * gscale;
+            v += partial[(int64_t)s * count + i];
         if (out_bf16)
             ((uint16_t*)out)[i] = f32_to_bf16(v);
         else

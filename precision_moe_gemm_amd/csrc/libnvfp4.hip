@@ -153,75 +153,108 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
         return NVFP4_ERR_SHAPE;
     gemm_stream_kernel<MODE><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
     nvfp4_status s = launch_status();
-    if (s != NVFP4_OK || p.ksplit <= 1)
-        return s;
+    if (s != NVFP4_OK || p.ksplit <= 1 || MODE != kModeDense)
+        return s;  // grouped down: the combine adds the planes
     const int64_t count = p.M * p.N;
     const unsigned rb = (unsigned)std::min<int64_t>(2048, ceil_div(count, 256));
-    splitk_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, count, p.a_global, p.w_global, p.out,
-                                             p.out_bf16);
+    splitk_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, count, p.out, p.out_bf16);
     return launch_status();
 }
 
-// Tile configurations: (BM, BN, waves).  Chosen by the rows an expert (or
-// the dense A) holds on average.
-template <int MODE>
-nvfp4_status dispatch_gemm(GemmArgs p, int64_t rows_avg, int64_t total_rows, int experts,
-                           int32_t* tile_off_ws, hipStream_t st)
+// Dense GEMM tile configurations (BM, BN, waves), chosen by the rows of A.
+nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
 {
     if (p.ksplit < 1)
         p.ksplit = 1;
-    if (use_stream_gemm(rows_avg, p.K)) {
-        p.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? kSkBN / 2 : kSkBN);
-        int64_t m_ub;
-        if (MODE == kModeDense) {
-            m_ub = ceil_div(total_rows, kSkBM);
-        } else {
-            p.ksplit = 1;
-            tile_offsets_kernel<<<1, 1024, 0, st>>>(p.offsets, experts, kSkBM, tile_off_ws);
-            nvfp4_status s = launch_status();
-            if (s != NVFP4_OK)
-                return s;
-            p.tile_off = tile_off_ws;
-            m_ub = ceil_div(total_rows, kSkBM) + experts;
-        }
-        return launch_stream_gemm<MODE>(p, m_ub, st);
+    if (use_stream_gemm(p.M, p.K)) {
+        p.n_tiles = ceil_div(p.N, kSkBN);
+        return launch_stream_gemm<kModeDense>(p, ceil_div(p.M, kSkBM), st);
     }
     p.ksplit = 1;
-    int bm;
-    if (rows_avg >= 256)
-        bm = 256;
-    else if (rows_avg >= 96)
-        bm = 128;
-    else if (rows_avg > 32)
-        bm = 64;
-    else
-        bm = 32;
-    const int bn = 256;
-    const int64_t ncols = (MODE == kModeGateUp) ? p.N : p.N;  // output columns
-    const int64_t per_tile_cols = (MODE == kModeGateUp) ? bn / 2 : bn;
-    p.n_tiles = ceil_div(ncols, per_tile_cols);
-    int64_t m_ub;
-    if (MODE == kModeDense) {
-        m_ub = ceil_div(total_rows, bm);
-    } else {
-        tile_offsets_kernel<<<1, 1024, 0, st>>>(p.offsets, experts, bm, tile_off_ws);
-        nvfp4_status s = launch_status();
+    p.n_tiles = ceil_div(p.N, 256);
+    if (p.M >= 256)
+        return launch_gemm<256, 256, 2, 2, kModeDense>(p, ceil_div(p.M, 256), st);
+    if (p.M >= 96)
+        return launch_gemm<128, 256, 2, 2, kModeDense>(p, ceil_div(p.M, 128), st);
+    if (p.M > 32)
+        return launch_gemm<64, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 64), st);
+    return launch_gemm<32, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 32), st);
+}
+
+// K split of the grouped down projection of a tiny batch (a dense MLP run as
+// a one-expert layer, or a handful of tokens over few experts): every tile is
+// a 16-row weight-streaming tile and split s writes its scaled partial sums
+// to plane s of y, which the combine adds in split order.
+int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
+{
+    const int64_t np = T * k;
+    if (np <= 0 || np > 256 || I % kSkBK != 0)
+        return 1;
+    const int64_t tiles = std::min<int64_t>(E, ceil_div(np, kSkBM)) * ceil_div(H, kSkBN);
+    if (tiles >= 512)
+        return 1;
+    int64_t s = 768 / tiles;
+    s = std::min<int64_t>(s, I / kSkBK / 4);
+    s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * H * 4));
+    return (int)std::max<int64_t>(1, s);
+}
+
+// Grouped projections: plan the tiles of every class on the device, then
+// launch each class (largest tiles first).  With p.ksplit > 1 (down only)
+// every tile is a 16-row streaming tile.
+template <int MODE>
+nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_rows, int experts,
+                              int32_t* plan, hipStream_t st)
+{
+    const bool stream_ok = p.K % kSkBK == 0;
+    const int small_bm = stream_ok ? kSkBM : 32;
+    const int all_small = p.ksplit > 1 ? 1 : 0;
+    if (p.ksplit < 1 || !stream_ok || MODE != kModeDown)
+        p.ksplit = 1;
+    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
+    nvfp4_status s = launch_status();
+    if (s != NVFP4_OK)
+        return s;
+    const int64_t E1 = experts + 1;
+    auto cls = [&](int c) {
+        GemmArgs q = p;
+        q.tile_off = plan + 3 * c * E1;
+        q.row_base = q.tile_off + E1;
+        q.row_lim = q.tile_off + 2 * E1;
+        return q;
+    };
+    const int64_t big_cols = MODE == kModeGateUp ? 128 : 256;
+    if (!all_small) {
+        GemmArgs q = cls(0);
+        q.ksplit = 1;
+        q.n_tiles = ceil_div(p.N, big_cols);
+        s = launch_gemm<256, 256, 2, 2, MODE>(q, total_rows / 128 + 1, st);
         if (s != NVFP4_OK)
             return s;
-        p.tile_off = tile_off_ws;
-        m_ub = ceil_div(total_rows, bm) + experts;
+        q = cls(1);
+        q.ksplit = 1;
+        q.n_tiles = ceil_div(p.N, big_cols);
+        s = launch_gemm<128, 256, 2, 2, MODE>(q, std::min<int64_t>(experts, total_rows / 65 + 1), st);
+        if (s != NVFP4_OK)
+            return s;
     }
-    switch (bm) {
-    case 256: return launch_gemm<256, 256, 2, 2, MODE>(p, m_ub, st);
-    case 128: return launch_gemm<128, 256, 2, 2, MODE>(p, m_ub, st);
-    case 64: return launch_gemm<64, 256, 1, 4, MODE>(p, m_ub, st);
-    default: return launch_gemm<32, 256, 1, 4, MODE>(p, m_ub, st);
+    GemmArgs q = cls(3);
+    // class 3: at most 4 tiles per expert (64 rows; 16 tiles with all_small,
+    // <= 256 rows), each holding at least one row
+    const int64_t m_small = std::min<int64_t>((int64_t)experts * (all_small ? ceil_div(256, kSkBM) : 4),
+                                              total_rows);
+    if (stream_ok) {
+        q.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? kSkBN / 2 : kSkBN);
+        return launch_stream_gemm<MODE>(q, m_small, st);
     }
+    q.ksplit = 1;
+    q.n_tiles = ceil_div(p.N, big_cols);
+    return launch_gemm<32, 256, 1, 4, MODE>(q, m_small, st);
 }
 
 // ---------------------------------------------------------------- MoE ws
 struct RouteLayout {
-    size_t hist, base, tot, offsets, tile_gu, tile_dn, end;
+    size_t hist, base, tot, offsets, plan_gu, plan_dn, end;
 };
 
 RouteLayout route_layout(int64_t npairs, int32_t E)
@@ -233,8 +266,8 @@ RouteLayout route_layout(int64_t npairs, int32_t E)
     L.base = o; o = align256(o + sizeof(int32_t) * nchunks * E);
     L.tot = o; o = align256(o + sizeof(int32_t) * E);
     L.offsets = o; o = align256(o + sizeof(int32_t) * (E + 1));
-    L.tile_gu = o; o = align256(o + sizeof(int32_t) * (E + 1));
-    L.tile_dn = o; o = align256(o + sizeof(int32_t) * (E + 1));
+    L.plan_gu = o; o = align256(o + sizeof(int32_t) * 3 * kPlanClasses * (E + 1));
+    L.plan_dn = o; o = align256(o + sizeof(int32_t) * 3 * kPlanClasses * (E + 1));
     L.end = o;
     return L;
 }
@@ -261,7 +294,7 @@ MoeLayout moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
     L.hq_p = o; o = align256(o + (size_t)(np * I / 2));
     L.hq_s = o; o = align256(o + (size_t)(np * I / 16));
     L.gh = o; o = align256(o + sizeof(float));
-    L.y = o; o = align256(o + sizeof(float) * (size_t)(np * H));
+    L.y = o; o = align256(o + sizeof(float) * (size_t)(np * H) * moe_down_ksplit(T, k, E, H, I));
     L.end = o;
     return L;
 }
@@ -501,7 +534,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
         p.ksplit = ksplit;
         p.partial = (float*)ws;
     }
-    return dispatch_gemm<kModeDense>(p, A->rows, A->rows, 1, nullptr, S(stream));
+    return dispatch_dense(p, S(stream));
 }
 
 nvfp4_status nvfp4_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
@@ -574,18 +607,18 @@ nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, cons
     p.w_global = w13->global;
     p.K = H;
     p.N = I;
-    p.offsets = offsets;
     p.perm = perm;
     p.topk = k;
     p.experts = E;
     p.out = h;
     p.h_amax = h_amax;
-    return dispatch_gemm<kModeGateUp>(p, T * k / E, T * k, E, at<int32_t>(ws, L.tile_gu), S(stream));
+    p.ksplit = 1;
+    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_gu), S(stream));
 }
 
-nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
-                            int32_t E, const nvfp4_tensor* w2, float* y, void* ws, size_t ws_bytes,
-                            void* stream)
+static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
+                                  int32_t E, const nvfp4_tensor* w2, float* y, int ksplit, void* ws,
+                                  size_t ws_bytes, hipStream_t st)
 {
     int64_t H = 0, I = 0;
     nvfp4_status s = check_experts(nullptr, w2, E, &H, &I);
@@ -613,11 +646,20 @@ nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int6
     p.w_global = w2->global;
     p.K = I;
     p.N = H;
-    p.offsets = offsets;
+    p.M = T * k;
     p.topk = k;
     p.experts = E;
     p.out = y;
-    return dispatch_gemm<kModeDown>(p, T * k / E, T * k, E, at<int32_t>(ws, L.tile_dn), S(stream));
+    p.ksplit = ksplit;
+    p.partial = y;
+    return dispatch_grouped<kModeDown>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_dn), st);
+}
+
+nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
+                            int32_t E, const nvfp4_tensor* w2, float* y, void* ws, size_t ws_bytes,
+                            void* stream)
+{
+    return moe_down_impl(hq, offsets, T, k, E, w2, y, 1, ws, ws_bytes, S(stream));
 }
 
 nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
@@ -629,7 +671,8 @@ nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* 
         return NVFP4_OK;
     if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 16))
         return NVFP4_ERR_INVALID_ARG;
-    combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, (u32x4*)out);
+    combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, 1, 0,
+                                                                           (u32x4*)out);
     return launch_status();
 }
 
@@ -683,13 +726,18 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         s = quantize_impl(h, T * k, I, I, kGlobalAmaxWord, hmax, &hq, 0, nullptr, st);
     if (s != NVFP4_OK)
         return s;
-    // 5. down
+    // 5. down (K split into planes of y for tiny batches)
     float* y = at<float>(ws, L.y);
-    s = nvfp4_moe_down(&hq, offsets, T, k, E, w2, y, ws, L.r.end, stream);
+    const int ksplit = moe_down_ksplit(T, k, E, H, I);
+    s = moe_down_impl(&hq, offsets, T, k, E, w2, y, ksplit, ws, L.r.end, st);
     if (s != NVFP4_OK)
         return s;
-    // 6. combine
-    return nvfp4_moe_combine(y, inv, w, T, k, H, out, stream);
+    // 6. combine (adds the planes of y in order)
+    if (!w || H % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
+                                                                   (u32x4*)out);
+    return launch_status();
 }
 
 nvfp4_status nvfp4_kv_quant(const void* k, const void* v, int64_t n, int64_t heads, int64_t tok_offset,

@@ -170,10 +170,89 @@ tile_offsets_kernel(const int32_t* __restrict__ offsets, int E, int bm, int32_t*
         tile_off[E] = total;
 }
 
-// out[t, 8c..8c+8) = bf16(sum_j w[t,j] * y[inv[t*k+j], 8c..8c+8))
+// Tile plan of a grouped projection.  Each expert's rows are cut into full
+// 256-row tiles plus one remainder of r = rows % 256 rows, and the remainder
+// goes to the smallest tile class that holds it, so that little MFMA work is
+// spent on padding rows when the tokens per expert are skewed:
+//   class 0: 256-row tiles (the full tiles, and remainders r > 128)
+//   class 1: 128-row tiles (64 < r <= 128)
+//   class 2: unused (kept so that class indices match the tile shapes)
+//   class 3: `small_bm`-row tiles (r <= 64; small_bm is 16 or 32)
+// With `all_small`, every expert's rows go to class 3 instead.
+// For class c, plan + 3 c (E + 1) holds tile_off[E + 1] (exclusive prefix of
+// the class's tiles per expert), then row_base[E + 1] and row_lim[E + 1]:
+// tile i of expert e covers rows [row_base[e] + i bm, min(+bm, row_lim[e])).
+constexpr int kPlanClasses = 4;
+
+NVFP4_DEV void plan_expert(int32_t lo, int32_t hi, int small_bm, int all_small, int32_t tiles[4],
+                           int32_t base[4], int32_t lim[4])
+{
+    if (all_small) {
+        // every row in class-3 tiles (K-split streaming projections)
+        for (int j = 0; j < 3; j++) {
+            tiles[j] = 0;
+            base[j] = lo;
+            lim[j] = lo;
+        }
+        tiles[3] = (hi - lo + small_bm - 1) / small_bm;
+        base[3] = lo;
+        lim[3] = hi;
+        return;
+    }
+    const int32_t rows = hi - lo, nf = rows >> 8, r = rows & 255;
+    const int32_t tail = lo + (nf << 8);
+    const int c = r > 128 ? 0 : r > 64 ? 1 : 3;
+    tiles[0] = nf + (c == 0 && r > 0 ? 1 : 0);
+    base[0] = lo;
+    lim[0] = c == 0 ? hi : tail;
+    for (int j = 1; j < 4; j++) {
+        base[j] = tail;
+        lim[j] = c == j ? hi : tail;
+    }
+    tiles[1] = c == 1 ? 1 : 0;
+    tiles[2] = c == 2 ? 1 : 0;
+    tiles[3] = c == 3 ? (r + small_bm - 1) / small_bm : 0;
+}
+
+__global__ void __launch_bounds__(1024)
+moe_plan_kernel(const int32_t* __restrict__ offsets, int E, int small_bm, int all_small,
+                int32_t* __restrict__ plan)
+{
+    __shared__ int32_t lds16[16];
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per;
+    int32_t cnt[4] = {0, 0, 0, 0};
+    for (int e = e0; e < e0 + per && e < E; e++) {
+        int32_t t[4], b[4], l[4];
+        plan_expert(offsets[e], offsets[e + 1], small_bm, all_small, t, b, l);
+        for (int c = 0; c < 4; c++)
+            cnt[c] += t[c];
+    }
+    int32_t run[4], total[4];
+    for (int c = 0; c < 4; c++)
+        run[c] = block_exclusive_scan(cnt[c], lds16, &total[c]);
+    for (int e = e0; e < e0 + per && e < E; e++) {
+        int32_t t[4], b[4], l[4];
+        plan_expert(offsets[e], offsets[e + 1], small_bm, all_small, t, b, l);
+        for (int c = 0; c < 4; c++) {
+            int32_t* pc = plan + 3 * c * (E + 1);
+            pc[e] = run[c];
+            pc[(E + 1) + e] = b[c];
+            pc[2 * (E + 1) + e] = l[c];
+            run[c] += t[c];
+        }
+    }
+    if (threadIdx.x == 0)
+        for (int c = 0; c < 4; c++)
+            plan[3 * c * (E + 1) + E] = total[c];
+}
+
+// out[t, 8c..8c+8) = bf16(sum_j w[t,j] * y[inv[t*k+j], 8c..8c+8)), where
+// y is the sum (in plane order) of `planes` partial planes `plane` floats apart
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
-               const float* __restrict__ w, int64_t T, int k, int64_t H, u32x4* __restrict__ out)
+               const float* __restrict__ w, int64_t T, int k, int64_t H, int planes, int64_t plane,
+               u32x4* __restrict__ out)
 {
     const int64_t groups = H / 8;
     const int64_t total = T * groups;
@@ -187,7 +266,12 @@ combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
                 continue;
             const float wt = w[t * k + j];
             const float4_t* src = (const float4_t*)(y + (int64_t)q * H + 8 * c);
-            const float4_t v0 = src[0], v1 = src[1];
+            float4_t v0 = src[0], v1 = src[1];
+            for (int sp = 1; sp < planes; sp++) {
+                const float4_t* ps = (const float4_t*)((const float*)src + sp * plane);
+                v0 += ps[0];
+                v1 += ps[1];
+            }
             acc[0] += wt * v0.x; acc[1] += wt * v0.y; acc[2] += wt * v0.z; acc[3] += wt * v0.w;
             acc[4] += wt * v1.x; acc[5] += wt * v1.y; acc[6] += wt * v1.z; acc[7] += wt * v1.w;
         }
