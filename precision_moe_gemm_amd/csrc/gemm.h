@@ -133,6 +133,10 @@ gemm_kernel(GemmArgs p)
     // written one stage ahead (ring of 2)
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kRowF16Bytes];
     __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][BN * kRowF16Bytes];
+    // scale bytes: each decoded row's 16 bytes for a group of 4 stages are
+    // fetched in one request and parked here, dword q of slot (i, tid) at
+    // [buf][q][i * NT + tid]; only the thread that parked them reads them
+    __shared__ uint32_t lds_sc[2][4][NT * RPT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -217,7 +221,6 @@ gemm_kernel(GemmArgs p)
         }
     }
     u32x4 creg[2][RPT][2];
-    uint32_t sreg[2][RPT];
     const int64_t nstages = K / kBK;
     auto load_stage = [&](int64_t st, int set) {
 #pragma unroll
@@ -225,15 +228,49 @@ gemm_kernel(GemmArgs p)
             const u32x4* c = (const u32x4*)(csrc[i] + st * kStageCodeBytes);
             creg[set][i][0] = c[0];
             creg[set][i][1] = c[1];
-            sreg[set][i] = *(const uint32_t*)(ssrc[i] + st * kStageScaleBytes);
         }
+    };
+    // scale dwords of stages [4 G, 4 G + 4): one 16-byte load per row, or,
+    // for a last group that is not whole, one clamped dword per stage
+    u32x4 tsc[RPT];
+    auto load_scales = [&](int64_t grp) {
+        const int64_t st0 = 4 * grp;
+        if (st0 + 4 <= nstages) {
+#pragma unroll
+            for (int i = 0; i < RPT; i++)
+                tsc[i] = *(const u32x4*)(ssrc[i] + st0 * kStageScaleBytes);
+        } else {
+            const int64_t last = nstages - 1;
+#pragma unroll
+            for (int i = 0; i < RPT; i++) {
+                tsc[i].x = *(const uint32_t*)(ssrc[i] + (st0 < last ? st0 : last) * kStageScaleBytes);
+                tsc[i].y = *(const uint32_t*)(ssrc[i] + (st0 + 1 < last ? st0 + 1 : last) * kStageScaleBytes);
+                tsc[i].z = *(const uint32_t*)(ssrc[i] + (st0 + 2 < last ? st0 + 2 : last) * kStageScaleBytes);
+                tsc[i].w = *(const uint32_t*)(ssrc[i] + (st0 + 3 < last ? st0 + 3 : last) * kStageScaleBytes);
+            }
+        }
+    };
+    auto park_scales = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            lds_sc[buf][0][i * NT + tid] = tsc[i].x;
+            lds_sc[buf][1][i * NT + tid] = tsc[i].y;
+            lds_sc[buf][2][i * NT + tid] = tsc[i].z;
+            lds_sc[buf][3][i * NT + tid] = tsc[i].w;
+        }
+    };
+    uint32_t scw[RPT];  // scale dwords of the stage being decoded
+    auto read_scales = [&](int64_t st) {
+#pragma unroll
+        for (int i = 0; i < RPT; i++)
+            scw[i] = lds_sc[(st >> 2) & 1][st & 3][i * NT + tid];
     };
     // decode part q (of 4: the 16-element block q) of the stage in register
     // set `set` into tile buffer `buf`
     auto decode_part = [&](int set, int buf, int part) {
 #pragma unroll
         for (int i = 0; i < RPT; i++) {
-            const uint32_t sw = sreg[set][i];
+            const uint32_t sw = scw[i];
             const half2_t s2 = part < 2 ? scales2<0>(sw) : scales2<1>(sw);
             const _Float16 sc = (part & 1) ? s2.y : s2.x;
             const u32x4 cv = creg[set][i][part >> 1];
@@ -277,8 +314,12 @@ gemm_kernel(GemmArgs p)
             fw[slot][j] = *(const half8_t*)(tw + woff[j] + 16 * ((2 * kk + g) ^ sw_w));
     };
 
-    // prologue: stage 0 decoded into buffers 0, packed stage 1 in registers
+    // prologue: scales of stages 0..3 parked, stage 0 decoded into buffers
+    // 0, packed stage 1 in registers
+    load_scales(0);
+    park_scales(0);
     load_stage(0, 0);
+    read_scales(0);
 #pragma unroll
     for (int q = 0; q < 4; q++)
         decode_part(0, 0, q);
@@ -287,16 +328,22 @@ gemm_kernel(GemmArgs p)
     read_frags(lds_a[0], lds_w[0], 0, 0);
 
     // one stage: MFMAs on buffers CUR (stage s) interleaved with decoding
-    // the packed stage s+1 (register set CUR ^ 1) into buffers CUR ^ 1.  CUR
-    // is a compile-time constant so both register sets stay in fixed
-    // registers.
-    auto stage = [&](int64_t s, auto cur_tag) {
-        constexpr int cur = decltype(cur_tag)::value, nxt = cur ^ 1;
+    // the packed stage s+1 (register set CUR ^ 1) into buffers CUR ^ 1.
+    // Q = s mod 4 and CUR = Q mod 2 are compile-time constants, so every
+    // register set stays in fixed registers.
+    auto stage = [&](int64_t s, auto q_tag) {
+        constexpr int Q = decltype(q_tag)::value;
+        constexpr int cur = Q & 1, nxt = cur ^ 1;
         // refill the register set stage s used (decoded last iteration);
         // past the end reload the last stage (harmless, never decoded)
         load_stage(s + 2 < nstages ? s + 2 : nstages - 1, cur);
+        if (Q == 2)
+            load_scales((s + 2) >> 2);  // the group that starts at stage s+2
         // issue those loads first: they have the whole stage to land
-        __builtin_amdgcn_sched_group_barrier(0x020, 3 * RPT, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x020, Q == 2 ? 3 * RPT : 2 * RPT, 0);  // VMEM read
+        if (Q == 3)
+            park_scales(((s + 1) >> 2) & 1);  // its buffer was last read four stages ago
+        read_scales(s + 1);
         const uint8_t* ta = lds_a[cur];
         const uint8_t* tw = lds_w[cur];
 #pragma unroll
@@ -329,12 +376,18 @@ gemm_kernel(GemmArgs p)
         read_frags(lds_a[nxt], lds_w[nxt], 0, 0);
     };
     int64_t s = 0;
-    for (; s + 1 < nstages; s += 2) {
+    for (; s + 3 < nstages; s += 4) {
         stage(s, IntC<0>{});
         stage(s + 1, IntC<1>{});
+        stage(s + 2, IntC<2>{});
+        stage(s + 3, IntC<3>{});
     }
     if (s < nstages)
         stage(s, IntC<0>{});
+    if (s + 1 < nstages)
+        stage(s + 1, IntC<1>{});
+    if (s + 2 < nstages)
+        stage(s + 2, IntC<2>{});
 
     // ---- epilogue --------------------------------------------------------
     const float gscale = *p.a_global * p.w_global[e];
