@@ -33,7 +33,9 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_moe384_T16384.json")
-GEMM_SOURCES = ["precision_moe_gemm_amd/csrc/gemm.h", "precision_moe_gemm_amd/csrc/common.h"]
+# sources that shape the grouped gate_up launch (kernels, tile plan, class dispatch)
+GEMM_SOURCES = ["precision_moe_gemm_amd/csrc/gemm.h", "precision_moe_gemm_amd/csrc/common.h",
+                "precision_moe_gemm_amd/csrc/moe.h", "precision_moe_gemm_amd/csrc/libnvfp4.hip"]
 
 
 def log(msg):
@@ -156,11 +158,13 @@ def main():
     gu_ms = time_loop(gate_up, max(5, args.steps), stream)
     gu_flops = 2.0 * T * k * (2 * I) * H
     gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
-    traffic = load_traffic(1)
+    traffic = load_traffic(1)  # HBM bytes per gate_up call, from the committed counter runs
     roofline = {
         "bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(gu_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
-        "kernel": "grouped gate_up GEMM + SwiGLU (gemm_kernel, f16 MFMA 32x32x16)",
+        "kernel": "grouped gate_up GEMM + SwiGLU, one nvfp4_moe_gate_up call: tile plan, then "
+                  "256-row and 128-row gemm_kernel classes (f16 MFMA 32x32x16) and the 16-row "
+                  "gemm_stream_kernel class (f16 MFMA 16x16x32)",
         "launch_ms": round(gu_ms, 4),
         "algorithmic_flops_per_launch": gu_flops,
         "frac_of_fp8_peak": round(gu_tflops / PEAK_FP8_TFLOPS, 4),
