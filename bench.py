@@ -369,11 +369,25 @@ def breakdown(args):
 
     write_all()
     ms_w = time_loop(write_all, 3, st)
+    # the same 128 chunk writes replayed from a captured HIP graph, as a
+    # serving loop issues them (no host overhead per chunk)
+    side = torch.cuda.Stream()
+    side.wait_stream(st)
+    with torch.cuda.stream(side):
+        write_all()
+    st.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        write_all()
+    graph.replay()
+    ms_wg = time_loop(graph.replay, 5, st)
     ms_w1 = time_loop(lambda: nv.nvfp4_kv_quant(kk, vv, 0, kc, vc, c5.heads), it, st)
     ko = torch.empty((c5.tokens, c5.heads, c5.dim), dtype=torch.bfloat16, device=dev)
     ms_r = time_loop(lambda: nv.nvfp4_kv_dequant(kc, vc, c5.heads, 0, c5.tokens, torch.bfloat16), it, st)
     nel = 2 * c5.tokens * c5.heads * c5.dim
     res["kv_262144x4x256"] = {"write_128_chunks_ms": round(ms_w, 4), "write_chunked_GBps": gbs(2.5625 * nel, ms_w),
+                              "write_128_chunks_graph_ms": round(ms_wg, 4),
+                              "write_chunked_graph_GBps": gbs(2.5625 * nel, ms_wg),
                               "write_single_call_ms": round(ms_w1, 4),
                               "write_single_GBps": gbs(2.5625 * nel, ms_w1),
                               "read_ms": round(ms_r, 4), "read_GBps": gbs(2.5625 * nel, ms_r),

@@ -266,11 +266,14 @@ def nvfp4_kv_quant(k: torch.Tensor | None, v: torch.Tensor | None, tok_offset: i
 
 
 def nvfp4_kv_dequant(k_cache: NVFP4Tensor, v_cache: NVFP4Tensor, heads: int, tok_begin: int, n: int,
-                     dtype=torch.bfloat16, want_k=True, want_v=True):
+                     dtype=torch.bfloat16, want_k=True, want_v=True, k_out=None, v_out=None):
     D = k_cache.cols
     dev = k_cache.device
-    ko = torch.empty((n, heads, D), dtype=dtype, device=dev) if want_k else None
-    vo = torch.empty((n, heads, D), dtype=dtype, device=dev) if want_v else None
+    ko = vo = None
+    if want_k:
+        ko = k_out if k_out is not None else torch.empty((n, heads, D), dtype=dtype, device=dev)
+    if want_v:
+        vo = v_out if v_out is not None else torch.empty((n, heads, D), dtype=dtype, device=dev)
     code = _lib.BF16 if dtype == torch.bfloat16 else _lib.F32
     kc, vc = k_cache.c(), v_cache.c()
     _check(_lib.load().nvfp4_kv_dequant(ctypes.byref(kc), ctypes.byref(vc), heads, tok_begin, n,

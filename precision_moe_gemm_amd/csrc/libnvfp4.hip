@@ -59,7 +59,7 @@ nvfp4_status launch_quantize(QuantArgs a, int ntensors, hipStream_t st)
     const int64_t nblk = a.rows * a.blocks_per_row;
     if (nblk == 0)
         return NVFP4_OK;
-    dim3 grid(stream_grid(nblk, 4096), ntensors);
+    dim3 grid(stream_grid(ceil_div(2 * nblk, 8), 4096), ntensors);  // 8 half-blocks per thread per trip
     quantize_kernel<<<grid, kQuantThreads, 0, st>>>(a);
     return launch_status();
 }
@@ -433,13 +433,13 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dty
     const int64_t nblk = in->batch * in->rows * bpr;
     if (nblk == 0 || in->rows == 0)
         return NVFP4_OK;
-    const unsigned grid = stream_grid(nblk, 8192);
+    const unsigned grid = stream_grid(ceil_div(2 * nblk, 8), 8192);  // 8 half-blocks per thread per trip
     if (dtype == NVFP4_BF16)
         dequantize_kernel<true><<<grid, kQuantThreads, 0, S(stream)>>>(
-            (const u32x2*)in->packed, in->scales, in->global, nblk, bpr, in->rows, 0, out);
+            (const uint32_t*)in->packed, in->scales, in->global, nblk, in->rows * bpr, 0, out);
     else
         dequantize_kernel<false><<<grid, kQuantThreads, 0, S(stream)>>>(
-            (const u32x2*)in->packed, in->scales, in->global, nblk, bpr, in->rows, 0, out);
+            (const uint32_t*)in->packed, in->scales, in->global, nblk, in->rows * bpr, 0, out);
     return launch_status();
 }
 
@@ -487,9 +487,12 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0, int64
     s = launch_status();
     if (s != NVFP4_OK)
         return s;
-    const unsigned parts2 = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, ceil_div(per_mat, 256)));
+    // 16 blocks per thread when every 16-block group is 16-byte aligned
+    const int vec16 = per_mat % 16 == 0 && aligned(e8m0, 16) && aligned(out->scales, 16) && aligned(ws, 16);
+    const int64_t items = vec16 ? per_mat / 16 : per_mat;
+    const unsigned parts2 = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, ceil_div(items, 256)));
     remap_scales_kernel<<<dim3(parts2, (unsigned)batch), kMxThreads, 0, S(stream)>>>(
-        e8m0, flags, per_mat, pmax, pmin, (int)parts, (uint16_t*)out->scales, out->global);
+        e8m0, flags, per_mat, pmax, pmin, (int)parts, (uint16_t*)out->scales, out->global, vec16);
     return launch_status();
 }
 
@@ -806,15 +809,15 @@ nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v
             continue;
         const int64_t bpr = src[j]->cols / 16;
         const int64_t nblk = n * heads * bpr;
-        const unsigned grid = stream_grid(nblk, 8192);
+        const unsigned grid = stream_grid(ceil_div(2 * nblk, 8), 8192);
         if (dtype == NVFP4_BF16)
             dequantize_kernel<true><<<grid, kQuantThreads, 0, S(stream)>>>(
-                (const u32x2*)src[j]->packed, src[j]->scales, src[j]->global, nblk, bpr, src[j]->rows,
-                tok_begin * heads, dst[j]);
+                (const uint32_t*)src[j]->packed, src[j]->scales, src[j]->global, nblk, src[j]->rows * bpr,
+                tok_begin * heads * bpr, dst[j]);
         else
             dequantize_kernel<false><<<grid, kQuantThreads, 0, S(stream)>>>(
-                (const u32x2*)src[j]->packed, src[j]->scales, src[j]->global, nblk, bpr, src[j]->rows,
-                tok_begin * heads, dst[j]);
+                (const uint32_t*)src[j]->packed, src[j]->scales, src[j]->global, nblk, src[j]->rows * bpr,
+                tok_begin * heads * bpr, dst[j]);
         nvfp4_status s = launch_status();
         if (s != NVFP4_OK)
             return s;

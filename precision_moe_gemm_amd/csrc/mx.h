@@ -117,12 +117,27 @@ remap_scan_kernel(const u32x4* __restrict__ mx, const uint8_t* __restrict__ e8m0
     }
 }
 
+// E4M3 byte for the block with E8M0 byte `eb` (2^(eb-127)) relative to the
+// window top emax: 2^((eb-127) - emax + 8), or 0x01 for an all-zero block
+// (flag 0), or 0 for a scale out of range (the error is raised elsewhere).
+NVFP4_DEV uint32_t remap_scale_code(uint32_t eb, uint32_t flag, int emax)
+{
+    if (!flag)
+        return 0x01;
+    const int d = ((int)eb - 127) - emax + 8;  // in [-9, 8] when in range
+    if (eb == 255 || d < -9)
+        return 0;
+    if (d < -6)
+        return 1u << (d + 9);           // subnormal E4M3 powers of two
+    return (uint32_t)(d + 7) << 3;      // normal E4M3 2^d
+}
+
 // ---- remap pass 2: scale bytes and the global -----------------------------
 __global__ void __launch_bounds__(kMxThreads)
 remap_scales_kernel(const uint8_t* __restrict__ e8m0, const uint8_t* __restrict__ nz_flags,
                     int64_t blocks_per_mat, const int* __restrict__ part_max,
                     const int* __restrict__ part_min, int nparts,
-                    uint16_t* __restrict__ scales, float* __restrict__ globals)
+                    uint16_t* __restrict__ scales, float* __restrict__ globals, int vec16)
 {
     const int64_t mat = blockIdx.y;
     int emax = kNoExp, emin = -kNoExp;
@@ -141,17 +156,34 @@ remap_scales_kernel(const uint8_t* __restrict__ e8m0, const uint8_t* __restrict_
     const uint8_t* flags = nz_flags + mat * blocks_per_mat;
     uint16_t* sc = scales + mat * blocks_per_mat;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < blocks_per_mat; b += stride) {
-        uint32_t code = 0x01;  // zero block
-        if (flags[b]) {
-            const int d = ((int)ex[b] - 127) - emax + 8;  // in [-9, 8] when in range
-            if (ex[b] == 255 || d < -9)
-                code = 0;      // cannot be represented: scale 0, error raised above
-            else if (d < -6)
-                code = 1u << (d + 9);           // subnormal E4M3 powers of two
-            else
-                code = (uint32_t)(d + 7) << 3;  // normal E4M3 2^d
+    const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (vec16) {
+        // 16 blocks per thread: 16 exponent bytes and 16 flags in, 32 scale bytes out
+        const int64_t groups = blocks_per_mat >> 4;
+        for (int64_t gi = first; gi < groups; gi += stride) {
+            const int64_t b = gi << 4;
+            const u32x4 ew = *(const u32x4*)(ex + b);
+            const u32x4 fw = *(const u32x4*)(flags + b);
+            uint32_t o[8];
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                const uint32_t e4 = w == 0 ? ew.x : w == 1 ? ew.y : w == 2 ? ew.z : ew.w;
+                const uint32_t f4 = w == 0 ? fw.x : w == 1 ? fw.y : w == 2 ? fw.z : fw.w;
+                uint32_t c[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    c[j] = remap_scale_code((e4 >> (8 * j)) & 0xFF, (f4 >> (8 * j)) & 0xFF, emax);
+                o[2 * w] = (c[0] | (c[0] << 8)) | ((c[1] | (c[1] << 8)) << 16);
+                o[2 * w + 1] = (c[2] | (c[2] << 8)) | ((c[3] | (c[3] << 8)) << 16);
+            }
+            u32x4* d = (u32x4*)(sc + b);
+            d[0] = (u32x4){o[0], o[1], o[2], o[3]};
+            d[1] = (u32x4){o[4], o[5], o[6], o[7]};
         }
+        return;
+    }
+    for (int64_t b = first; b < blocks_per_mat; b += stride) {
+        const uint32_t code = remap_scale_code(ex[b], flags[b], emax);
         sc[b] = (uint16_t)(code | (code << 8));
     }
 }

@@ -66,27 +66,31 @@ NVFP4_DEV float load_global(int src, const void* gsrc, int nparts, uint32_t* lds
     return global_from_amax(__uint_as_float(m));
 }
 
-// Encode one 16-element block held as two u32x4 of bf16 bits.
-// Returns the two code dwords; *scale_out gets the E4M3 byte.
-NVFP4_DEV u32x2 encode_block(u32x4 lo, u32x4 hi, float G, float six_g, uint32_t* scale_out)
+// Scale of one 16-element block from its bf16 magnitude bits `am` (the
+// block amax): *sc gets the E4M3 byte, the return value is the reciprocal
+// r = 1 / (s * G) the codes are taken with (0 when s = 0).
+NVFP4_DEV float block_scale(uint32_t am, float G, float six_g, uint32_t* sc)
 {
-    uint32_t am = absmax_bits8(lo);
-    uint32_t am2 = absmax_bits8(hi);
-    am = am > am2 ? am : am2;
     const float ab = __uint_as_float(am << 16);
     const float s_real = ab / six_g;
-    const uint32_t sc = e4m3_encode(s_real);
-    *scale_out = sc;
-    const float s = e4m3_decode(sc);
+    *sc = e4m3_encode(s_real);
+    const float s = e4m3_decode(*sc);
     float r = 0.0f;                       // scale 0: every code becomes +-0
-    if (sc != 0) {
+    if (*sc != 0) {
         const float p = s * G;
         r = 1.0f / p;
     }
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    float y[16];
+    return r;
+}
+
+// Eight bf16 values (one u32x4) times r -> eight E2M1 codes (one dword,
+// element 2j in the low nibble of byte j).
+NVFP4_DEV uint32_t encode_half(u32x4 v, float r)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < 4; i++) {
         y[2 * i] = bf16_lo(w[i]) * r;
         y[2 * i + 1] = bf16_hi(w[i]) * r;
     }
@@ -94,22 +98,18 @@ NVFP4_DEV u32x2 encode_block(u32x4 lo, u32x4 hi, float G, float six_g, uint32_t*
         // s * G underflowed: x * inf is +-inf (code 6) except 0 * inf, which
         // is taken as a zero code with the sign of x.
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+        for (int i = 0; i < 4; i++) {
+            const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
             y[2 * i] = a == 0.0f ? a : y[2 * i];
             y[2 * i + 1] = b == 0.0f ? b : y[2 * i + 1];
         }
     }
-    uint32_t c0 = 0, c1 = 0;
-    c0 = FP4_PACK2(c0, y[0], y[1], 0);
-    c0 = FP4_PACK2(c0, y[2], y[3], 1);
-    c0 = FP4_PACK2(c0, y[4], y[5], 2);
-    c0 = FP4_PACK2(c0, y[6], y[7], 3);
-    c1 = FP4_PACK2(c1, y[8], y[9], 0);
-    c1 = FP4_PACK2(c1, y[10], y[11], 1);
-    c1 = FP4_PACK2(c1, y[12], y[13], 2);
-    c1 = FP4_PACK2(c1, y[14], y[15], 3);
-    return (u32x2){c0, c1};
+    uint32_t c = 0;
+    c = FP4_PACK2(c, y[0], y[1], 0);
+    c = FP4_PACK2(c, y[2], y[3], 1);
+    c = FP4_PACK2(c, y[4], y[5], 2);
+    c = FP4_PACK2(c, y[6], y[7], 3);
+    return c;
 }
 
 // ---- pass 2: block quantize ---------------------------------------------
@@ -133,68 +133,116 @@ quantize_kernel(QuantArgs a)
 {
     __shared__ uint32_t red[16];
     const int j = blockIdx.y;
+    const int64_t bpr = a.blocks_per_row;
+    const int64_t nhalf = 2 * a.rows * bpr;
+    const u32x4* __restrict__ x = a.x[j];
+    uint32_t* __restrict__ packed = (uint32_t*)(a.packed[j] + a.row_off[j] * bpr);
+    uint8_t* __restrict__ scales = a.scales[j] + a.row_off[j] * bpr;
+    const bool flat = a.ld_chunks == 2 * bpr;
+    // work item = half a block (8 elements, one 16-byte chunk): lanes 2j and
+    // 2j+1 hold the two halves of a block and share its max with one lane
+    // swap, so loads and code stores are contiguous per instruction.  A
+    // workgroup takes kQU * 256 consecutive half-blocks per trip, all loads
+    // issued first.
+    constexpr int kQU = 8;
+    constexpr int64_t kChunk = (int64_t)kQU * kQuantThreads;
+    u32x4 v[kQU];
+    auto load_trip = [&](int64_t base) {
+#pragma unroll
+        for (int u = 0; u < kQU; u++) {
+            int64_t h = base + u * kQuantThreads + threadIdx.x;
+            h = h < nhalf ? h : nhalf - 1;
+            int64_t src = h;
+            if (!flat) {
+                const int64_t b = h >> 1, r = b / bpr;
+                src = r * a.ld_chunks + 2 * (b - r * bpr) + (h & 1);
+            }
+            v[u] = __builtin_nontemporal_load(x + src);  // read once
+        }
+    };
+    int64_t base = (int64_t)blockIdx.x * kChunk;
+    // the first trip's data is requested before the global scale, so the two
+    // memory latencies overlap (this matters for small writes such as a KV chunk)
+    if (base < nhalf)
+        load_trip(base);
     const float G = load_global(a.src[j], a.gsrc[j], a.nparts, red);
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.global_out[j])
         *a.global_out[j] = G;
     const float six_g = 6.0f * G;
-    const int64_t nblk = a.rows * a.blocks_per_row;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const u32x4* __restrict__ x = a.x[j];
-    u32x2* __restrict__ packed = a.packed[j] + a.row_off[j] * a.blocks_per_row;
-    uint8_t* __restrict__ scales = a.scales[j] + a.row_off[j] * a.blocks_per_row;
-    const bool flat = a.ld_chunks == 2 * a.blocks_per_row;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-        int64_t src;
-        if (flat) {
-            src = 2 * b;
-        } else {
-            int64_t r = b / a.blocks_per_row;
-            src = r * a.ld_chunks + 2 * (b - r * a.blocks_per_row);
+    for (; base < nhalf; base += (int64_t)gridDim.x * kChunk) {
+#pragma unroll
+        for (int u = 0; u < kQU; u++) {
+            const int64_t h = base + u * kQuantThreads + threadIdx.x;
+            uint32_t am = absmax_bits8(v[u]);
+            const uint32_t other = (uint32_t)__shfl_xor((int)am, 1, 64);
+            am = am > other ? am : other;
+            uint32_t sc;
+            const float r = block_scale(am, G, six_g, &sc);
+            const uint32_t code = encode_half(v[u], r);
+            if (h < nhalf) {
+                packed[h] = code;
+                if ((h & 1) == 0)
+                    scales[h >> 1] = (uint8_t)sc;
+            }
         }
-        const u32x4 lo = __builtin_nontemporal_load(x + src);
-        const u32x4 hi = __builtin_nontemporal_load(x + src + 1);
-        uint32_t sc;
-        const u32x2 codes = encode_block(lo, hi, G, six_g, &sc);
-        packed[b] = codes;
-        scales[b] = (uint8_t)sc;
+        const int64_t next = base + (int64_t)gridDim.x * kChunk;
+        if (next < nhalf)
+            load_trip(next);
     }
 }
 
 // ---- dequantize ------------------------------------------------------------
 // v = (e2m1 * s) * G in fp32; bf16 output rounds that value to nearest even.
-// rows_per_batch selects the global of each row's batch matrix.
+// Block gb = b + blk_off belongs to batch matrix gb / blocks_per_batch, whose
+// global applies.
 template <bool kBf16>
 __global__ void __launch_bounds__(kQuantThreads)
-dequantize_kernel(const u32x2* __restrict__ packed, const uint8_t* __restrict__ scales,
-                  const float* __restrict__ globals, int64_t nblk, int64_t blocks_per_row,
-                  int64_t rows_per_batch, int64_t row_off, void* __restrict__ out)
+dequantize_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                  const float* __restrict__ globals, int64_t nblk, int64_t blocks_per_batch,
+                  int64_t blk_off, void* __restrict__ out)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-        const int64_t gb = b + row_off * blocks_per_row;
-        const float G = globals[(gb / blocks_per_row) / rows_per_batch];
-        const u32x2 c = packed[gb];
-        const float s = e4m3_decode(scales[gb]);
-        float2_t q[8] = {FP4_TO_F32X2(c.x, 0), FP4_TO_F32X2(c.x, 1), FP4_TO_F32X2(c.x, 2),
-                         FP4_TO_F32X2(c.x, 3), FP4_TO_F32X2(c.y, 0), FP4_TO_F32X2(c.y, 1),
-                         FP4_TO_F32X2(c.y, 2), FP4_TO_F32X2(c.y, 3)};
-        float v[16];
+    // one matrix (the common case): one global, no per-block division
+    const bool single = blk_off + nblk <= blocks_per_batch;
+    const float G0 = globals[0];
+    // work item = half a block (8 codes, one code dword): lanes 2j and 2j+1
+    // take the two halves of a block, so every store instruction writes
+    // contiguous output.  A workgroup takes kDqUnroll * 256 consecutive
+    // half-blocks per trip, all loads issued first.
+    constexpr int kDqUnroll = 8;
+    constexpr int64_t kChunk = (int64_t)kDqUnroll * kQuantThreads;
+    const int64_t nhalf = 2 * nblk;
+    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < nhalf; base += (int64_t)gridDim.x * kChunk) {
+        uint32_t c[kDqUnroll], sb[kDqUnroll];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            v[2 * i] = (q[i].x * s) * G;
-            v[2 * i + 1] = (q[i].y * s) * G;
+        for (int u = 0; u < kDqUnroll; u++) {
+            const int64_t hb = base + u * kQuantThreads + threadIdx.x;
+            const int64_t gh = (hb < nhalf ? hb : nhalf - 1) + 2 * blk_off;
+            c[u] = packed[gh];
+            sb[u] = scales[gh >> 1];
         }
-        if (kBf16) {
-            u32x4* o = (u32x4*)out + 2 * b;
-            o[0] = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-            o[1] = (u32x4){pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                              pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15])};
-        } else {
-            float4_t* o = (float4_t*)out + 4 * b;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                o[i] = (float4_t){v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+        for (int u = 0; u < kDqUnroll; u++) {
+            const int64_t hb = base + u * kQuantThreads + threadIdx.x;
+            if (hb >= nhalf)
+                break;
+            const float G = single ? G0 : globals[((hb >> 1) + blk_off) / blocks_per_batch];
+            const float sc = e4m3_decode(sb[u]);
+            const float2_t q[4] = {FP4_TO_F32X2(c[u], 0), FP4_TO_F32X2(c[u], 1), FP4_TO_F32X2(c[u], 2),
+                                   FP4_TO_F32X2(c[u], 3)};
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                v[2 * i] = (q[i].x * sc) * G;
+                v[2 * i + 1] = (q[i].y * sc) * G;
+            }
+            if (kBf16) {
+                ((u32x4*)out)[hb] = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+            } else {
+                float4_t* o = (float4_t*)out + 2 * hb;
+                o[0] = (float4_t){v[0], v[1], v[2], v[3]};
+                o[1] = (float4_t){v[4], v[5], v[6], v[7]};
+            }
         }
     }
 }

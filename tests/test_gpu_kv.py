@@ -55,6 +55,43 @@ def test_chunked_writes_equal_whole_tensor(orc, order):
         np.testing.assert_array_equal(got, bref)
 
 
+def test_chunked_writes_replayed_from_a_graph(orc):
+    """The chunk writes captured once in a HIP graph, as a serving loop runs
+    them: every replay (caches cleared and unrelated eager work in between)
+    leaves exactly the bytes of the eager writes."""
+    kv = synth.KVCache(tokens=8192, chunk=2048)
+    k, v = kv.k(), kv.v()
+    gk, gv = _static_global(orc, k), _static_global(orc, v)
+    kd, vd = k.to(DEV), v.to(DEV)
+    ke, ve = _caches(kv.tokens, kv.heads, kv.dim, gk, gv)
+    kg, vg = _caches(kv.tokens, kv.heads, kv.dim, gk, gv)
+
+    def write_all(kc, vc):
+        for c0 in range(0, kv.tokens, kv.chunk):
+            nv.nvfp4_kv_quant(kd[c0:c0 + kv.chunk], vd[c0:c0 + kv.chunk], c0, kc, vc, kv.heads)
+
+    step("kv eager writes")
+    write_all(ke, ve)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        write_all(kg, vg)
+    torch.cuda.current_stream().wait_stream(side)
+    step("kv graph capture")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        write_all(kg, vg)
+    for rep in range(3):
+        for t in (kg.packed, kg.scales, vg.packed, vg.scales):
+            t.zero_()
+        nv.nvfp4_kv_dequant(ke, ve, kv.heads, 0, 512, torch.bfloat16)
+        step(f"kv graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in ((kg, ke), (vg, ve)):
+            assert torch.equal(a.packed, b.packed) and torch.equal(a.scales, b.scales), rep
+
+
 def test_full_context_write_read_sampled(orc):
     """262144 tokens x 4 heads x 256, 128 chunk writes then one full read;
     sampled rows checked against the oracle."""
