@@ -202,19 +202,25 @@ int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 // Grouped projections: plan the tiles of every class on the device, then
 // launch each class (largest tiles first).  With p.ksplit > 1 (down only)
 // every tile is a 16-row streaming tile.
+// Streaming tile rows of a grouped projection with reduction length K.
+int grouped_small_bm(int64_t K) { return K % kSkBK == 0 ? kSkBM : 32; }
+
 template <int MODE>
 nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_rows, int experts,
-                              int32_t* plan, hipStream_t st)
+                              int32_t* plan, bool plan_ready, hipStream_t st)
 {
     const bool stream_ok = p.K % kSkBK == 0;
-    const int small_bm = stream_ok ? kSkBM : 32;
+    const int small_bm = grouped_small_bm(p.K);
     const int all_small = p.ksplit > 1 ? 1 : 0;
     if (p.ksplit < 1 || !stream_ok || MODE != kModeDown)
         p.ksplit = 1;
-    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
-    nvfp4_status s = launch_status();
-    if (s != NVFP4_OK)
-        return s;
+    nvfp4_status s = NVFP4_OK;
+    if (!plan_ready) {
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
+        s = launch_status();
+        if (s != NVFP4_OK)
+            return s;
+    }
     const int64_t E1 = experts + 1;
     auto cls = [&](int c) {
         GemmArgs q = p;
@@ -224,14 +230,18 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
         return q;
     };
     const int64_t big_cols = MODE == kModeGateUp ? 128 : 256;
-    if (!all_small) {
+    // class 0 needs an expert with more than 128 rows, class 1 one with more
+    // than 64: skip launches that cannot have work
+    if (!all_small && total_rows > 128) {
         GemmArgs q = cls(0);
         q.ksplit = 1;
         q.n_tiles = ceil_div(p.N, big_cols);
         s = launch_gemm<256, 256, 2, 2, MODE>(q, total_rows / 128 + 1, st);
         if (s != NVFP4_OK)
             return s;
-        q = cls(1);
+    }
+    if (!all_small && total_rows > 64) {
+        GemmArgs q = cls(1);
         q.ksplit = 1;
         q.n_tiles = ceil_div(p.N, big_cols);
         s = launch_gemm<128, 256, 2, 2, MODE>(q, std::min<int64_t>(experts, total_rows / 65 + 1), st);
@@ -302,11 +312,22 @@ MoeLayout moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 template <typename T>
 inline T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
 
+// Route the T*k pairs.  Small batches take one workgroup, which can also
+// write the two tile plans (plan_gu / plan_dn non-null) for the fused layer.
 nvfp4_status route_impl(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
                         int32_t* offsets, int32_t* inv, void* ws, const RouteLayout& L,
-                        uint32_t* zero_word, hipStream_t st)
+                        uint32_t* zero_word, hipStream_t st, int32_t* plan_gu = nullptr,
+                        int small_bm_gu = 0, int32_t* plan_dn = nullptr, int small_bm_dn = 0,
+                        int all_small_dn = 0)
 {
     const int64_t np = T * k;
+    if (np <= kRouteSmall) {
+        route_small_kernel<<<1, 1024, 0, st>>>(ids, (int)np, E, offsets, perm, inv, zero_word, plan_gu,
+                                               small_bm_gu, plan_dn, small_bm_dn, all_small_dn);
+        return launch_status();
+    }
+    if (plan_gu || plan_dn)
+        return NVFP4_ERR_INVALID_ARG;  // plans come from the small route only
     const int64_t nchunks = ceil_div(np, kRouteChunk);
     if (np > 0) {
         route_hist_kernel<<<(unsigned)nchunks, kRouteChunk, sizeof(int32_t) * E, st>>>(
@@ -580,9 +601,10 @@ static nvfp4_status check_experts(const nvfp4_tensor* w13, const nvfp4_tensor* w
     return NVFP4_OK;
 }
 
-nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
-                               int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
-                               uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream)
+static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+                                     int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
+                                     uint32_t* h_amax, void* ws, size_t ws_bytes, bool plan_ready,
+                                     hipStream_t st)
 {
     int64_t H = 0, I = 0;
     nvfp4_status s = check_experts(w13, nullptr, E, &H, &I);
@@ -616,12 +638,19 @@ nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, cons
     p.out = h;
     p.h_amax = h_amax;
     p.ksplit = 1;
-    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_gu), S(stream));
+    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_gu), plan_ready, st);
+}
+
+nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+                               int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
+                               uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream)
+{
+    return moe_gate_up_impl(xq, perm, offsets, T, k, E, w13, h, h_amax, ws, ws_bytes, false, S(stream));
 }
 
 static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
                                   int32_t E, const nvfp4_tensor* w2, float* y, int ksplit, void* ws,
-                                  size_t ws_bytes, hipStream_t st)
+                                  size_t ws_bytes, bool plan_ready, hipStream_t st)
 {
     int64_t H = 0, I = 0;
     nvfp4_status s = check_experts(nullptr, w2, E, &H, &I);
@@ -655,14 +684,14 @@ static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets
     p.out = y;
     p.ksplit = ksplit;
     p.partial = y;
-    return dispatch_grouped<kModeDown>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_dn), st);
+    return dispatch_grouped<kModeDown>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_dn), plan_ready, st);
 }
 
 nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
                             int32_t E, const nvfp4_tensor* w2, float* y, void* ws, size_t ws_bytes,
                             void* stream)
 {
-    return moe_down_impl(hq, offsets, T, k, E, w2, y, 1, ws, ws_bytes, S(stream));
+    return moe_down_impl(hq, offsets, T, k, E, w2, y, 1, ws, ws_bytes, false, S(stream));
 }
 
 nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
@@ -704,8 +733,16 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     int32_t* inv = at<int32_t>(ws, L.inv);
     int32_t* offsets = at<int32_t>(ws, L.r.offsets);
     uint32_t* hmax = at<uint32_t>(ws, L.hmax);
-    // 1. route (also zeroes the h max word)
-    s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
+    // 1. route (also zeroes the h max word); a small batch routes in one
+    // workgroup that also plans both projections' tiles
+    const int ksplit = moe_down_ksplit(T, k, E, H, I);
+    const bool small = T * k <= kRouteSmall;
+    if (small)
+        s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
+                       grouped_small_bm(H), at<int32_t>(ws, L.r.plan_dn), grouped_small_bm(I),
+                       ksplit > 1 ? 1 : 0);
+    else
+        s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
     if (s != NVFP4_OK)
         return s;
     // 2. quantize x once
@@ -718,7 +755,7 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         return s;
     // 3. gate_up + SwiGLU
     void* h = at<void>(ws, L.h);
-    s = nvfp4_moe_gate_up(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, stream);
+    s = moe_gate_up_impl(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, small, st);
     if (s != NVFP4_OK)
         return s;
     // 4. quantize h over all T*k rows
@@ -731,8 +768,7 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         return s;
     // 5. down (K split into planes of y for tiny batches)
     float* y = at<float>(ws, L.y);
-    const int ksplit = moe_down_ksplit(T, k, E, H, I);
-    s = moe_down_impl(&hq, offsets, T, k, E, w2, y, ksplit, ws, L.r.end, st);
+    s = moe_down_impl(&hq, offsets, T, k, E, w2, y, ksplit, ws, L.r.end, small, st);
     if (s != NVFP4_OK)
         return s;
     // 6. combine (adds the planes of y in order)

@@ -214,17 +214,17 @@ NVFP4_DEV void plan_expert(int32_t lo, int32_t hi, int small_bm, int all_small, 
     tiles[3] = c == 3 ? (r + small_bm - 1) / small_bm : 0;
 }
 
-__global__ void __launch_bounds__(1024)
-moe_plan_kernel(const int32_t* __restrict__ offsets, int E, int small_bm, int all_small,
-                int32_t* __restrict__ plan)
+// The plan of all experts by one workgroup of 1024 threads; offs[e] and
+// offs[e + 1] bound expert e's rows (offs may be in LDS).
+NVFP4_DEV void plan_block(const int32_t* offs, int E, int small_bm, int all_small, int32_t* plan,
+                          int32_t* lds16)
 {
-    __shared__ int32_t lds16[16];
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
     int32_t cnt[4] = {0, 0, 0, 0};
     for (int e = e0; e < e0 + per && e < E; e++) {
         int32_t t[4], b[4], l[4];
-        plan_expert(offsets[e], offsets[e + 1], small_bm, all_small, t, b, l);
+        plan_expert(offs[e], offs[e + 1], small_bm, all_small, t, b, l);
         for (int c = 0; c < 4; c++)
             cnt[c] += t[c];
     }
@@ -233,7 +233,7 @@ moe_plan_kernel(const int32_t* __restrict__ offsets, int E, int small_bm, int al
         run[c] = block_exclusive_scan(cnt[c], lds16, &total[c]);
     for (int e = e0; e < e0 + per && e < E; e++) {
         int32_t t[4], b[4], l[4];
-        plan_expert(offsets[e], offsets[e + 1], small_bm, all_small, t, b, l);
+        plan_expert(offs[e], offs[e + 1], small_bm, all_small, t, b, l);
         for (int c = 0; c < 4; c++) {
             int32_t* pc = plan + 3 * c * (E + 1);
             pc[e] = run[c];
@@ -245,6 +245,84 @@ moe_plan_kernel(const int32_t* __restrict__ offsets, int E, int small_bm, int al
     if (threadIdx.x == 0)
         for (int c = 0; c < 4; c++)
             plan[3 * c * (E + 1) + E] = total[c];
+}
+
+__global__ void __launch_bounds__(1024)
+moe_plan_kernel(const int32_t* __restrict__ offsets, int E, int small_bm, int all_small,
+                int32_t* __restrict__ plan)
+{
+    __shared__ int32_t lds16[16];
+    plan_block(offsets, E, small_bm, all_small, plan, lds16);
+}
+
+// Routing of a small batch (at most kRouteSmall pairs) in one workgroup, with
+// the result of the chunked route above: counts in LDS, one scan, and each
+// pair's rank among the earlier pairs with the same id.  Optionally also
+// writes the tile plans of the two grouped projections (plan_gu, plan_dn)
+// and zeroes `zero_word`, so a small layer needs one launch for all of it.
+constexpr int kRouteSmall = 1024;
+
+__global__ void __launch_bounds__(1024)
+route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
+                   int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
+                   int32_t* plan_gu, int small_bm_gu, int32_t* plan_dn, int small_bm_dn, int all_small_dn)
+{
+    __shared__ int32_t sid[kRouteSmall];
+    __shared__ int32_t off[kMaxExperts + 1];
+    __shared__ int32_t lds16[16];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x)
+        off[e] = 0;
+    int32_t my = -1;
+    if (tid < npairs) {
+        my = ids[tid];
+        if (my < 0 || my >= E) {
+            raise_error(NVFP4_ERR_RANGE);
+            my = -1;
+        }
+    }
+    sid[tid] = my;
+    __syncthreads();
+    if (my >= 0)
+        atomicAdd(&off[my], 1);
+    __syncthreads();
+    // counts -> exclusive offsets, in place
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = tid * per;
+    int32_t local = 0;
+    for (int e = e0; e < e0 + per && e < E; e++)
+        local += off[e];
+    int32_t total;
+    int32_t run = block_exclusive_scan(local, lds16, &total);
+    for (int e = e0; e < e0 + per && e < E; e++) {
+        const int32_t c = off[e];
+        off[e] = run;
+        offsets[e] = run;
+        run += c;
+    }
+    if (tid == 0) {
+        off[E] = total;
+        offsets[E] = total;
+        if (zero_word)
+            *zero_word = 0;
+    }
+    __syncthreads();
+    if (tid < npairs) {
+        if (my < 0) {
+            inv[tid] = -1;
+        } else {
+            int32_t rank = 0;
+            for (int i = 0; i < tid; i++)
+                rank += sid[i] == my;
+            const int32_t q = off[my] + rank;
+            perm[q] = tid;
+            inv[tid] = q;
+        }
+    }
+    if (plan_gu)
+        plan_block(off, E, small_bm_gu, 0, plan_gu, lds16);
+    if (plan_dn)
+        plan_block(off, E, small_bm_dn, all_small_dn, plan_dn, lds16);
 }
 
 // out[t, 8c..8c+8) = bf16(sum_j w[t,j] * y[inv[t*k+j], 8c..8c+8)), where
