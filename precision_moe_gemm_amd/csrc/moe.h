@@ -43,8 +43,11 @@ route_hist_kernel(const int32_t* __restrict__ ids, int64_t npairs, int E, int32_
 }
 
 // Block-wide exclusive scan of one int per thread (blockDim.x <= 1024, a
-// multiple of 64).  Returns the exclusive prefix; *total gets the sum.
-NVFP4_DEV int32_t block_exclusive_scan(int32_t v, int32_t* lds16, int32_t* total)
+// multiple of 64): .x = the exclusive prefix, .y = the block total.
+struct ScanResult {
+    int32_t prefix, total;
+};
+NVFP4_DEV ScanResult block_exclusive_scan(int32_t v, int32_t* lds16)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int32_t incl = v;
@@ -64,8 +67,7 @@ NVFP4_DEV int32_t block_exclusive_scan(int32_t v, int32_t* lds16, int32_t* total
         base += w < wid ? lds16[w] : 0;
         all += lds16[w];
     }
-    *total = all;
-    return base + incl - v;
+    return ScanResult{base + incl - v, all};
 }
 
 // 2a. One workgroup per expert e: exclusive scan of hist[.][e] over chunks
@@ -81,8 +83,9 @@ route_expert_scan_kernel(const int32_t* __restrict__ hist, int64_t nchunks, int 
     int32_t local = 0;
     for (int64_t c = c0; c < c0 + per && c < nchunks; c++)
         local += hist[c * E + e];
-    int32_t total;
-    int32_t run = block_exclusive_scan(local, lds16, &total);
+    const ScanResult sr = block_exclusive_scan(local, lds16);
+    const int32_t total = sr.total;
+    int32_t run = sr.prefix;
     for (int64_t c = c0; c < c0 + per && c < nchunks; c++) {
         const int32_t v = hist[c * E + e];
         base[c * E + e] = run;
@@ -104,8 +107,9 @@ route_offsets_kernel(const int32_t* __restrict__ tot, int E, int32_t* __restrict
     int32_t local = 0;
     for (int e = e0; e < e0 + per && e < E; e++)
         local += tot[e];
-    int32_t total;
-    int32_t run = block_exclusive_scan(local, lds16, &total);
+    const ScanResult sr = block_exclusive_scan(local, lds16);
+    const int32_t total = sr.total;
+    int32_t run = sr.prefix;
     for (int e = e0; e < e0 + per && e < E; e++) {
         offsets[e] = run;
         run += tot[e];
@@ -160,8 +164,9 @@ tile_offsets_kernel(const int32_t* __restrict__ offsets, int E, int bm, int32_t*
     int32_t local = 0;
     for (int e = e0; e < e0 + per && e < E; e++)
         local += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-    int32_t total;
-    int32_t run = block_exclusive_scan(local, lds16, &total);
+    const ScanResult sr = block_exclusive_scan(local, lds16);
+    const int32_t total = sr.total;
+    int32_t run = sr.prefix;
     for (int e = e0; e < e0 + per && e < E; e++) {
         tile_off[e] = run;
         run += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
@@ -184,34 +189,28 @@ tile_offsets_kernel(const int32_t* __restrict__ offsets, int E, int bm, int32_t*
 // tile i of expert e covers rows [row_base[e] + i bm, min(+bm, row_lim[e])).
 constexpr int kPlanClasses = 4;
 
-NVFP4_DEV void plan_expert(int32_t lo, int32_t hi, int small_bm, int all_small, int32_t tiles[4],
-                           int32_t base[4], int32_t lim[4])
+// Class C's share of expert rows [lo, hi): its tile count, row base and row
+// limit (scalars, so the callers' unrolled class loops stay in registers).
+struct ClassPlan {
+    int32_t tiles, base, lim;
+};
+template <int C>
+NVFP4_DEV ClassPlan plan_class(int32_t lo, int32_t hi, int small_bm, int all_small)
 {
     if (all_small) {
         // every row in class-3 tiles (K-split streaming projections)
-        for (int j = 0; j < 3; j++) {
-            tiles[j] = 0;
-            base[j] = lo;
-            lim[j] = lo;
-        }
-        tiles[3] = (hi - lo + small_bm - 1) / small_bm;
-        base[3] = lo;
-        lim[3] = hi;
-        return;
+        if (C == 3)
+            return ClassPlan{(hi - lo + small_bm - 1) / small_bm, lo, hi};
+        return ClassPlan{0, lo, lo};
     }
     const int32_t rows = hi - lo, nf = rows >> 8, r = rows & 255;
     const int32_t tail = lo + (nf << 8);
     const int c = r > 128 ? 0 : r > 64 ? 1 : 3;
-    tiles[0] = nf + (c == 0 && r > 0 ? 1 : 0);
-    base[0] = lo;
-    lim[0] = c == 0 ? hi : tail;
-    for (int j = 1; j < 4; j++) {
-        base[j] = tail;
-        lim[j] = c == j ? hi : tail;
-    }
-    tiles[1] = c == 1 ? 1 : 0;
-    tiles[2] = c == 2 ? 1 : 0;
-    tiles[3] = c == 3 ? (r + small_bm - 1) / small_bm : 0;
+    if (C == 0)
+        return ClassPlan{nf + (c == 0 && r > 0 ? 1 : 0), lo, c == 0 ? hi : tail};
+    if (C == 3)
+        return ClassPlan{c == 3 ? (r + small_bm - 1) / small_bm : 0, tail, c == 3 ? hi : tail};
+    return ClassPlan{c == C ? 1 : 0, tail, c == C ? hi : tail};
 }
 
 // The plan of all experts by one workgroup of 1024 threads; offs[e] and
@@ -221,30 +220,39 @@ NVFP4_DEV void plan_block(const int32_t* offs, int E, int small_bm, int all_smal
 {
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
-    int32_t cnt[4] = {0, 0, 0, 0};
+    int32_t cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
     for (int e = e0; e < e0 + per && e < E; e++) {
-        int32_t t[4], b[4], l[4];
-        plan_expert(offs[e], offs[e + 1], small_bm, all_small, t, b, l);
-        for (int c = 0; c < 4; c++)
-            cnt[c] += t[c];
+        const int32_t lo = offs[e], hi = offs[e + 1];
+        cnt0 += plan_class<0>(lo, hi, small_bm, all_small).tiles;
+        cnt1 += plan_class<1>(lo, hi, small_bm, all_small).tiles;
+        cnt2 += plan_class<2>(lo, hi, small_bm, all_small).tiles;
+        cnt3 += plan_class<3>(lo, hi, small_bm, all_small).tiles;
     }
-    int32_t run[4], total[4];
-    for (int c = 0; c < 4; c++)
-        run[c] = block_exclusive_scan(cnt[c], lds16, &total[c]);
+    const ScanResult s0 = block_exclusive_scan(cnt0, lds16);
+    const ScanResult s1 = block_exclusive_scan(cnt1, lds16);
+    const ScanResult s2 = block_exclusive_scan(cnt2, lds16);
+    const ScanResult s3 = block_exclusive_scan(cnt3, lds16);
+    int32_t run0 = s0.prefix, run1 = s1.prefix, run2 = s2.prefix, run3 = s3.prefix;
+    auto put = [&](int c, int e, const ClassPlan& cp, int32_t& run) {
+        int32_t* pc = plan + 3 * c * (E + 1);
+        pc[e] = run;
+        pc[(E + 1) + e] = cp.base;
+        pc[2 * (E + 1) + e] = cp.lim;
+        run += cp.tiles;
+    };
     for (int e = e0; e < e0 + per && e < E; e++) {
-        int32_t t[4], b[4], l[4];
-        plan_expert(offs[e], offs[e + 1], small_bm, all_small, t, b, l);
-        for (int c = 0; c < 4; c++) {
-            int32_t* pc = plan + 3 * c * (E + 1);
-            pc[e] = run[c];
-            pc[(E + 1) + e] = b[c];
-            pc[2 * (E + 1) + e] = l[c];
-            run[c] += t[c];
-        }
+        const int32_t lo = offs[e], hi = offs[e + 1];
+        put(0, e, plan_class<0>(lo, hi, small_bm, all_small), run0);
+        put(1, e, plan_class<1>(lo, hi, small_bm, all_small), run1);
+        put(2, e, plan_class<2>(lo, hi, small_bm, all_small), run2);
+        put(3, e, plan_class<3>(lo, hi, small_bm, all_small), run3);
     }
-    if (threadIdx.x == 0)
-        for (int c = 0; c < 4; c++)
-            plan[3 * c * (E + 1) + E] = total[c];
+    if (threadIdx.x == 0) {
+        plan[E] = s0.total;
+        plan[3 * (E + 1) + E] = s1.total;
+        plan[6 * (E + 1) + E] = s2.total;
+        plan[9 * (E + 1) + E] = s3.total;
+    }
 }
 
 __global__ void __launch_bounds__(1024)
@@ -292,8 +300,9 @@ route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* 
     int32_t local = 0;
     for (int e = e0; e < e0 + per && e < E; e++)
         local += off[e];
-    int32_t total;
-    int32_t run = block_exclusive_scan(local, lds16, &total);
+    const ScanResult sr = block_exclusive_scan(local, lds16);
+    const int32_t total = sr.total;
+    int32_t run = sr.prefix;
     for (int e = e0; e < e0 + per && e < E; e++) {
         const int32_t c = off[e];
         off[e] = run;
