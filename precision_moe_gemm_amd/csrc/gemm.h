@@ -117,6 +117,141 @@ NVFP4_DEV float silu_f(float g)
     return g / (1.0f + __expf(-g));
 }
 
+// Output tile of a prefill-class workgroup: expert, A-side rows
+// [row_begin, row_end) (rows of A, or list positions when grouped) and the
+// column tile.  False for surplus workgroups.
+struct TileCoord {
+    int e;
+    int64_t row_begin, row_end, nt;
+};
+template <int BM, int MODE>
+NVFP4_DEV bool tile_coord(const GemmArgs& p, TileCoord& tc)
+{
+    // XCD-aware: consecutive ids go round-robin over 8 XCDs, so each XCD
+    // takes a contiguous range of logical tiles
+    const int64_t m_act = MODE == kModeDense ? p.m_tiles : p.tile_off[p.experts];
+    const int64_t bid = xcd_item(m_act * p.n_tiles);
+    if (bid < 0)
+        return false;
+    const int64_t mt = bid / p.n_tiles;
+    tc.nt = bid - mt * p.n_tiles;
+    tc.e = 0;
+    if (MODE == kModeDense) {
+        if (mt >= p.m_tiles)
+            return false;
+        tc.row_begin = mt * BM;
+        tc.row_end = tc.row_begin + BM < p.M ? tc.row_begin + BM : p.M;
+    } else {
+        if (mt >= p.tile_off[p.experts])
+            return false;
+        int lo = 0, hi = p.experts - 1;  // largest e with tile_off[e] <= mt
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.tile_off[mid] <= mt)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        tc.e = lo;
+        tc.row_begin = p.row_base[lo] + (mt - p.tile_off[lo]) * BM;
+        const int64_t eend = p.row_lim[lo];
+        tc.row_end = tc.row_begin + BM < eend ? tc.row_begin + BM : eend;
+    }
+    return true;
+}
+
+// Row of A that tile row r reads (padding rows repeat a valid row and are
+// never stored); gate_up gathers token rows through the permutation.
+template <int MODE>
+NVFP4_DEV int64_t tile_a_row(const GemmArgs& p, const TileCoord& tc, int r)
+{
+    int64_t q = tc.row_begin + r;
+    if (q >= tc.row_end)
+        q = tc.row_begin;
+    if (MODE == kModeGateUp)
+        return p.perm[q] / p.topk;
+    return q;
+}
+
+// Row of W (within the expert) that W-tile row r reads.  For gate_up, wave
+// column group wn holds TN/2 gate rows then the matching TN/2 up rows, so a
+// lane's gate and up accumulators cover the same output column.
+template <int BN, int TN, int MODE>
+NVFP4_DEV int64_t tile_w_row(const GemmArgs& p, const TileCoord& tc, int r)
+{
+    if (MODE == kModeGateUp) {
+        const int wn = r / TN, rr = r % TN;
+        const int64_t base = tc.nt * (BN / 2) + wn * (TN / 2);
+        return rr < TN / 2 ? base + rr : p.N + base + (rr - TN / 2);
+    }
+    const int64_t n = tc.nt * BN + r;
+    return n < p.N ? n : p.N - 1;
+}
+
+// Epilogue of a 32x32-fragment wave tile: lane holds column lane % 32 and
+// rows (i % 4) + 8 (i / 4) + 4 (lane / 32) of each fragment.
+template <int BN, int WM, int WN, int TM, int TN, int FM, int FN, int MODE>
+NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&acc)[FM][FN], int wave_m,
+                          int wave_n, int lane)
+{
+    const float gscale = *p.a_global * p.w_global[tc.e];
+    const int ncol = lane & 31;
+    const int rsub = 4 * (lane >> 5);
+    const int64_t wrow0 = tc.row_begin + wave_m * TM;  // first output row of this wave
+    const int rows_left = (int)(tc.row_end - wrow0);
+    const int ld = (int)p.N;
+    if (MODE == kModeGateUp) {
+        const int64_t col0 = tc.nt * (BN / 2) + wave_n * (TN / 2) + ncol;
+        uint16_t* h = (uint16_t*)p.out + wrow0 * p.N + col0;
+        uint32_t hmax = 0;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
+                if (rr < rows_left) {
+#pragma unroll
+                    for (int j = 0; j < FN / 2; j++) {
+                        const float gg = acc[i][j][r] * gscale;
+                        const float uu = acc[i][j + FN / 2][r] * gscale;
+                        const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+                        h[rr * ld + j * 32] = hb;
+                        const uint32_t mag = hb & 0x7FFFu;
+                        hmax = hmax > mag ? hmax : mag;
+                    }
+                }
+            }
+        }
+        hmax = wave_max_u32(hmax);
+        if (lane == 0 && hmax != 0)
+            atomicMax(p.h_amax, hmax << 16);
+    } else {
+        const int64_t col0 = tc.nt * BN + wave_n * TN + ncol;
+        const bool bf16_out = MODE == kModeDense && p.out_bf16;
+        float* of = (float*)p.out + wrow0 * p.N + col0;
+        uint16_t* ob = (uint16_t*)p.out + wrow0 * p.N + col0;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
+                if (rr < rows_left) {
+#pragma unroll
+                    for (int j = 0; j < FN; j++) {
+                        if (col0 + j * 32 < p.N) {
+                            const float v = acc[i][j][r] * gscale;
+                            if (bf16_out)
+                                ob[rr * ld + j * 32] = f32_to_bf16(v);
+                            else
+                                of[rr * ld + j * 32] = v;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(GemmArgs p)
@@ -142,63 +277,18 @@ gemm_kernel(GemmArgs p)
     const int lane = tid & 63, wave = tid >> 6;
     const int wave_m = wave / WN, wave_n = wave % WN;
 
-    // ---- tile assignment (XCD-aware: consecutive ids go round-robin over 8
-    // XCDs, so give each XCD a contiguous range of logical tiles) ----------
-    const int64_t m_act = MODE == kModeDense ? p.m_tiles : p.tile_off[p.experts];
-    const int64_t bid = xcd_item(m_act * p.n_tiles);
-    if (bid < 0)
+    TileCoord tc;
+    if (!tile_coord<BM, MODE>(p, tc))
         return;
-    const int64_t mt = bid / p.n_tiles;
-    const int64_t nt = bid - mt * p.n_tiles;
-
-    int e = 0;
-    int64_t row_begin, row_end;  // A-side rows of this tile (list positions or rows)
-    if (MODE == kModeDense) {
-        if (mt >= p.m_tiles)
-            return;
-        row_begin = mt * BM;
-        row_end = row_begin + BM < p.M ? row_begin + BM : p.M;
-    } else {
-        if (mt >= p.tile_off[p.experts])
-            return;
-        int lo = 0, hi = p.experts - 1;  // largest e with tile_off[e] <= mt
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.tile_off[mid] <= mt)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        e = lo;
-        row_begin = p.row_base[e] + (mt - p.tile_off[e]) * BM;
-        const int64_t eend = p.row_lim[e];
-        row_end = row_begin + BM < eend ? row_begin + BM : eend;
-    }
+    const int e = tc.e;
 
     const int64_t K = p.K;
     const int64_t kpb = K / 2, kpsb = K / 16;  // packed / scale bytes per row
     const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
     const uint8_t* wp = p.w_packed + (int64_t)e * w_rows * kpb;
     const uint8_t* wsc = p.w_scales + (int64_t)e * w_rows * kpsb;
-
-    auto a_row_of = [&](int r) -> int64_t {
-        int64_t q = row_begin + r;
-        if (q >= row_end)
-            q = row_begin;  // padding rows repeat a valid row; never stored
-        if (MODE == kModeGateUp)
-            return p.perm[q] / p.topk;
-        return q;
-    };
-    auto w_row_of = [&](int r) -> int64_t {
-        if (MODE == kModeGateUp) {
-            // wave column group wn holds gate rows then the matching up rows
-            const int wn = r / TN, rr = r % TN;
-            const int64_t base = nt * (BN / 2) + wn * (TN / 2);
-            return rr < TN / 2 ? base + rr : p.N + base + (rr - TN / 2);
-        }
-        const int64_t n = nt * BN + r;
-        return n < p.N ? n : p.N - 1;
-    };
+    auto a_row_of = [&](int r) -> int64_t { return tile_a_row<MODE>(p, tc, r); };
+    auto w_row_of = [&](int r) -> int64_t { return tile_w_row<BN, TN, MODE>(p, tc, r); };
 
     // ---- rows this thread decodes from packed codes ----------------------
     const uint8_t* csrc[RPT];
@@ -350,30 +440,51 @@ gemm_kernel(GemmArgs p)
         for (int kk = 0; kk < 4; kk++) {
             const int sl = kk & 1;
             // fragments of the next k-step first, fenced so the scheduler
-            // cannot sink them next to their use
+            // cannot sink them next to their use; the last k-step reads the
+            // first fragments of stage s+1 (complete since the barrier)
             if (kk < 3)
                 read_frags(ta, tw, kk + 1, sl ^ 1);
+            else
+                read_frags(lds_a[nxt], lds_w[nxt], 0, sl ^ 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fw[sl][j], acc[i][j], 0, 0, 0);
-            // decode 1/4 of the next stage (the last iteration decodes stale
-            // registers into a buffer nobody reads again)
-            decode_part(nxt, nxt, kk);
+            // the next stage is decoded during the first three k-steps (the
+            // last stage decodes stale registers into a buffer nobody reads)
+            if (kk < 2)
+                decode_part(nxt, nxt, kk);
+            if (kk == 2) {
+                decode_part(nxt, nxt, 2);
+                decode_part(nxt, nxt, 3);
+            }
             // interleave the decode VALU work and its stores between MFMAs
+            if (kk < 2) {
 #pragma unroll
-            for (int m = 0; m < FM * FN; m++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
-                if (m % 4 == 3)
-                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                for (int m = 0; m < FM * FN; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+                    if (m % 4 == 3)
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                }
+            } else if (kk == 2) {
+#pragma unroll
+                for (int m = 0; m < FM * FN; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);      // VALU
+                    if (m % 2 == 1)
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
+            // stage s+1 is fully written and stage s's last fragments are in
+            // registers: one barrier, then the last k-step's MFMAs cover the
+            // latency of the first reads of stage s+1
+            if (kk == 2)
+                __syncthreads();
         }
-        __syncthreads();
-        read_frags(lds_a[nxt], lds_w[nxt], 0, 0);
     };
     int64_t s = 0;
     for (; s + 3 < nstages; s += 4) {
@@ -389,66 +500,369 @@ gemm_kernel(GemmArgs p)
     if (s + 2 < nstages)
         stage(s + 2, IntC<2>{});
 
-    // ---- epilogue --------------------------------------------------------
-    const float gscale = *p.a_global * p.w_global[e];
-    const int ncol = lane & 31;
-    const int rsub = 4 * (lane >> 5);
-    const int64_t wrow0 = row_begin + wave_m * TM;  // first output row of this wave
+    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane);
+}
 
-    if (MODE == kModeGateUp) {
-        const int64_t col0 = nt * (BN / 2) + wave_n * (TN / 2) + ncol;
-        uint16_t* h = (uint16_t*)p.out + wrow0 * p.N + col0;
-        const int ld = (int)p.N;
-        const int rows_left = (int)(row_end - wrow0);
-        uint32_t hmax = 0;
+// ---------------------------------------------------------------------------
+// Prefill mainloop with coalesced, direct-to-LDS code loads.
+//
+// Same tiles, MFMA and decode-once scheme as gemm_kernel (4 waves of
+// 128 x 128, v_mfma_f32_32x32x16_f16 on f16 LDS tiles), with the packed codes
+// moved by the LDS DMA path instead of through registers: a workgroup copies
+// the codes of a 128-element group of K for all its tile rows (64 bytes per
+// row, four lanes per row, 16 rows per instruction) straight into an LDS
+// staging buffer, two groups ahead of use.  Each f16 stage covers 32 K
+// elements; during stage s every thread reads its rows' 16 code bytes of
+// stage s+1 from the staging buffer, decodes them with their block scales
+// (held in registers, 16 bytes per row per 256 elements) and writes the f16
+// tile of stage s+1, while the waves run the two k-steps of stage s.  One
+// barrier per stage, placed between the two k-steps so the first fragments
+// of the next stage are read under the second k-step's MFMAs.
+// ---------------------------------------------------------------------------
+constexpr int kTFK = 32;             // K elements per f16 stage
+constexpr int kTFRow = kTFK * 2;     // f16 bytes per tile row per stage
+constexpr int kTGRow = 64;           // packed bytes per row per group (4 stages)
+constexpr int kTSRow = 16;           // scale bytes per row per scale group (8 stages)
+
+// Byte offset of 16-byte chunk c (of 4) of the 64-byte row r in an f16
+// tile or in the packed staging.  Rows are paired into 128-byte lines
+// (line r / 2 holds chunk c of row r in slot 4 (r % 2) + c) and the 8 slots
+// of line q are XOR-swizzled by (q ^ q / 2) mod 8: measured free of bank
+// conflicts both for reads and writes of 64 consecutive rows at one chunk
+// (staging reads, decode writes) and for MFMA fragment reads (32 rows, two
+// chunks); the plain 64-byte-row layouts measured were not.
+NVFP4_DEV int tline_sw(int r) { return ((r >> 1) ^ (r >> 2)) & 7; }
+NVFP4_DEV int tpos(int r, int c) { return 64 * (r & ~1) + 16 * ((4 * (r & 1) + c) ^ tline_sw(r)); }
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+NVFP4_DEV void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// wait until all of this wave's LDS operations are complete
+NVFP4_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier.  __syncthreads() would also wait for the LDS DMA
+// copies in flight (they count as LDS writes), which must stay in flight
+// across stages; their completion is awaited explicitly with wait_vm.
+NVFP4_DEV void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM, int BN, int MODE>
+__global__ void __launch_bounds__(256)
+gemm_tile_kernel(GemmArgs p)
+{
+    constexpr int WM = 2, WN = 2, NW = 4, NT = 256;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ROWS = BM + BN;
+    constexpr int NJ = (ROWS + 16 * NW - 1) / (16 * NW);  // staging copies per wave per group
+    constexpr int SROWS = NJ * NW * 16;                    // staged rows (>= ROWS)
+    constexpr int RPT = (ROWS + NT - 1) / NT;              // rows decoded per thread per stage
+    static_assert(BM % 32 == 0 && BN % 64 == 0, "tile shape");
+    static_assert(MODE != kModeGateUp || FN % 2 == 0, "gate_up pairs gate and up fragments");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds_f[2][ROWS * kTFRow];  // f16 tiles
+    // packed codes of groups with even / odd index (separate arrays, so the
+    // compiler sees that reading one does not wait for copies into the other)
+    __shared__ __attribute__((aligned(16))) uint8_t lds_p0[SROWS * kTGRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_p1[SROWS * kTGRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave / WN, wave_n = wave % WN;
+
+    TileCoord tc;
+    if (!tile_coord<BM, MODE>(p, tc))
+        return;
+    const int e = tc.e;
+    const int64_t K = p.K;
+    const int64_t kpb = K / 2, kpsb = K / 16;  // packed / scale bytes per row
+    const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
+    const uint8_t* wp = p.w_packed + (int64_t)e * w_rows * kpb;
+    const uint8_t* wsc = p.w_scales + (int64_t)e * w_rows * kpsb;
+    auto matrix_row = [&](int r) -> int64_t {
+        return r < BM ? tile_a_row<MODE>(p, tc, r) : tile_w_row<BN, TN, MODE>(p, tc, r - BM);
+    };
+
+    const int64_t nst = K / kTFK;      // f16 stages (even: K % 64 == 0)
+    const int64_t ngr = (nst + 3) >> 2;  // packed groups
+    const int64_t nsg = (nst + 7) >> 3;  // scale groups
+
+    // ---- staging copies: copy j of this wave fills LDS bytes
+    // [1024 (NJ wave + j), +1024), lane l writing 16 bytes at 16 l, which is
+    // line q = 8 (NJ wave + j) + l / 8, slot l % 8: the lane copies the
+    // (row, chunk) that tpos places there.  The 8 lanes of a line cover the
+    // 64 bytes of both its rows, so each copy reads 16 whole row segments.
+    int32_t srow[NJ];
+    int scq[NJ];
 #pragma unroll
-        for (int i = 0; i < FM; i++) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
-                if (rr < rows_left) {
-#pragma unroll
-                    for (int j = 0; j < FN / 2; j++) {
-                        const float gg = acc[i][j][r] * gscale;
-                        const float uu = acc[i][j + FN / 2][r] * gscale;
-                        const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
-                        h[rr * ld + j * 32] = hb;
-                        const uint32_t mag = hb & 0x7FFFu;
-                        hmax = hmax > mag ? hmax : mag;
-                    }
-                }
-            }
-        }
-        hmax = wave_max_u32(hmax);
-        if (lane == 0 && hmax != 0)
-            atomicMax(p.h_amax, hmax << 16);
-    } else {
-        const int64_t col0 = nt * BN + wave_n * TN + ncol;
-        const int ld = (int)p.N;
-        const int rows_left = (int)(row_end - wrow0);
-        const bool bf16_out = MODE == kModeDense && p.out_bf16;
-        float* of = (float*)p.out + wrow0 * p.N + col0;
-        uint16_t* ob = (uint16_t*)p.out + wrow0 * p.N + col0;
-#pragma unroll
-        for (int i = 0; i < FM; i++) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
-                if (rr < rows_left) {
-#pragma unroll
-                    for (int j = 0; j < FN; j++) {
-                        if (col0 + j * 32 < p.N) {
-                            const float v = acc[i][j][r] * gscale;
-                            if (bf16_out)
-                                ob[rr * ld + j * 32] = f32_to_bf16(v);
-                            else
-                                of[rr * ld + j * 32] = v;
-                        }
-                    }
-                }
-            }
-        }
+    for (int j = 0; j < NJ; j++) {
+        const int q = 8 * (NJ * wave + j) + (lane >> 3);
+        const int hc = (lane & 7) ^ ((q ^ (q >> 1)) & 7);  // 4 (r % 2) + c
+        int r = 2 * q + (hc >> 2);
+        if (r >= ROWS)
+            r = ROWS - 1;
+        srow[j] = (int32_t)matrix_row(r);
+        scq[j] = hc & 3;
     }
+    // copies [J0, J1) of group G into staging buffer BUF
+    auto issue_group = [&](int64_t G, auto buf_tag, auto j0_tag, auto j1_tag) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        constexpr int J0 = decltype(j0_tag)::value, J1 = decltype(j1_tag)::value;
+        const int64_t cb = G * kTGRow;
+        const int cvalid = (int)((kpb - cb) >> 4);  // whole chunks left in the row (>= 2)
+        uint8_t* dst = BUF ? lds_p1 : lds_p0;
+#pragma unroll
+        for (int j = J0; j < J1; j++) {
+            const bool is_a = 16 * (NJ * wave + j) < BM;  // uniform per copy
+            const int c = scq[j] < cvalid ? scq[j] : cvalid - 1;
+            const uint8_t* src = (is_a ? p.a_packed : wp) + (int64_t)srow[j] * kpb + cb + 16 * c;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + (NJ * wave + j) * 1024), 16,
+                                             0, 0);
+        }
+    };
+
+    // ---- rows this thread decodes, and their scale bytes (16 per row per
+    // scale group, in registers: the current group and the next)
+    int drow[RPT];
+    const uint8_t* ssrc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; i++) {
+        int r = tid + i * NT;
+        if (r >= ROWS)
+            r = ROWS - 1;  // surplus thread: decodes the last row again
+        drow[i] = r;
+        const int64_t mr = matrix_row(r);
+        ssrc[i] = (r < BM ? p.a_scales : wsc) + mr * kpsb;
+    }
+    u32x4 sc_cur[RPT], sc_nxt[RPT];
+    auto load_scales = [&](int64_t SG, u32x4 (&dst)[RPT]) {
+        const int64_t sb = SG * kTSRow;
+        if (sb + kTSRow <= kpsb) {
+#pragma unroll
+            for (int i = 0; i < RPT; i++)
+                dst[i] = *(const u32x4*)(ssrc[i] + sb);
+        } else {
+            // last group of a K that is not a multiple of 256: clamp dwords
+            const int64_t last = (kpsb >> 2) - 1;
+            const int64_t d0 = sb >> 2;
+#pragma unroll
+            for (int i = 0; i < RPT; i++) {
+                const uint32_t* q = (const uint32_t*)ssrc[i];
+                dst[i].x = q[d0 < last ? d0 : last];
+                dst[i].y = q[d0 + 1 < last ? d0 + 1 : last];
+                dst[i].z = q[d0 + 2 < last ? d0 + 2 : last];
+                dst[i].w = q[d0 + 3 < last ? d0 + 3 : last];
+            }
+        }
+    };
+
+    // decode f16 stage with index T (mod 8) of its scale group from the
+    // staged codes into f16 buffer FB
+    u32x4 dcodes[RPT];
+    auto stage_codes = [&](auto t_tag) {
+        constexpr int T = decltype(t_tag)::value;
+        const uint8_t* src = ((T >> 2) & 1) ? lds_p1 : lds_p0;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int r = drow[i];
+            dcodes[i] = *(const u32x4*)(src + tpos(r, T & 3));
+        }
+    };
+    auto decode_stage = [&](auto t_tag, const u32x4 (&sc)[RPT]) {
+        constexpr int T = decltype(t_tag)::value;
+        uint8_t* dst = lds_f[T & 1];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int r = drow[i];
+            const uint32_t sw = (T >> 1) == 0 ? sc[i].x : (T >> 1) == 1 ? sc[i].y : (T >> 1) == 2 ? sc[i].z : sc[i].w;
+            const half2_t s2 = (T & 1) ? scales2<1>(sw) : scales2<0>(sw);
+            *(u32x4*)(dst + tpos(r, 0)) = decode_chunk(dcodes[i].x, s2.x);
+            *(u32x4*)(dst + tpos(r, 1)) = decode_chunk(dcodes[i].y, s2.x);
+            *(u32x4*)(dst + tpos(r, 2)) = decode_chunk(dcodes[i].z, s2.y);
+            *(u32x4*)(dst + tpos(r, 3)) = decode_chunk(dcodes[i].w, s2.y);
+        }
+    };
+
+    float16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            acc[i][j] = (float16_t){};
+
+    const int frow = lane & 31;  // fragment row of this lane
+    const int g = lane >> 5;     // which 8 of the 16 K-elements of an MFMA step
+    // fragment rows of a lane differ by multiples of 32, which keeps the
+    // line swizzle and the row parity: one slot base per operand
+    const int ra = wave_m * TM + frow, rw = BM + wave_n * TN + frow;
+    const int aoff = 64 * (ra & ~1), woff = 64 * (rw & ~1);
+    const int ha = 4 * (ra & 1) + g, hw = 4 * (rw & 1) + g;
+    const int sw_a = tline_sw(ra), sw_w = tline_sw(rw);
+    half8_t fa[2][FM], fw[2][FN];
+    auto read_frags = [&](const uint8_t* t, int kk, int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            fa[slot][i] = *(const half8_t*)(t + aoff + 2048 * i + 16 * ((ha + 2 * kk) ^ sw_a));
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            fw[slot][j] = *(const half8_t*)(t + woff + 2048 * j + 16 * ((hw + 2 * kk) ^ sw_w));
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[slot][i], fw[slot][j], acc[i][j], 0, 0, 0);
+    };
+
+    // ---- prologue: scale groups 0 and 1 in registers, code groups 0 and 1
+    // staged, stage 0 decoded
+    load_scales(0, sc_cur);
+    load_scales(nsg > 1 ? 1 : 0, sc_nxt);
+    issue_group(0, IntC<0>{}, IntC<0>{}, IntC<NJ>{});
+    issue_group(ngr > 1 ? 1 : 0, IntC<1>{}, IntC<0>{}, IntC<NJ>{});
+    wait_vm<0>();
+    __syncthreads();
+    stage_codes(IntC<0>{});
+    decode_stage(IntC<0>{}, sc_cur);
+    stage_codes(IntC<1>{});
+    __syncthreads();
+    read_frags(lds_f[0], 0, 0);
+
+    // ---- stage s, T = s mod 8 (compile time): k-step 0 (fragments read
+    // last stage) with the decode of stage s+1, barrier, k-step 1 with the
+    // first fragment reads of stage s+1
+    auto stage = [&](int64_t s, auto t_tag) {
+        constexpr int T = decltype(t_tag)::value;
+        constexpr int CUR = T & 1;
+        constexpr int TN1 = (T + 1) & 7;  // stage s+1 mod 8
+        // Group G + 2 is copied into the staging buffer of group G (free
+        // from stage 4 G + 3 on) during stages 4 G + 3 .. 4 G + 5, three
+        // copies per stage spread between the MFMAs so the address unit never
+        // backs up, and awaited at stage 4 G + 6.  Past the last group the
+        // copies repeat the last group into the free buffer (harmless), which
+        // keeps the stage straight-line code.
+        constexpr bool CP = T != 2 && T != 6;
+        constexpr int PH = (T + 5) & 3;  // 0, 1, 2 for T = 3, 4, 5 (and 7, 0, 1)
+        constexpr int BUF = (T >= 3 && T <= 5) ? 0 : 1;
+        // copies [C0, C1) go between the first k-step's MFMAs, [C1, C2)
+        // between the second's (the first stage of a window: all three in
+        // its second k-step, which has no decode work)
+        constexpr int C0 = 3 * PH < NJ ? 3 * PH : NJ;
+        constexpr int C1 = PH == 0 ? C0 : (3 * PH + 1 < NJ ? 3 * PH + 1 : NJ);
+        constexpr int C2 = 3 * PH + 3 < NJ ? 3 * PH + 3 : NJ;
+        int64_t G2 = ((s + 1) >> 2) + 1;
+        G2 = G2 < ngr ? G2 : ngr - 1;
+        if (T == 4) {
+            // scales of the next group: the previous one moved in at T == 0
+            if ((s >> 3) + 1 < nsg)
+                load_scales((s >> 3) + 1, sc_nxt);
+        }
+        read_frags(lds_f[CUR], 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        if (T == 7)
+            decode_stage(IntC<TN1>{}, sc_nxt);
+        else
+            decode_stage(IntC<TN1>{}, sc_cur);
+        if (CP && C1 > C0)
+            issue_group(G2, IntC<BUF>{}, IntC<C0>{}, IntC<C1>{});
+#pragma unroll
+        for (int m = 0; m < FM * FN; m++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // VALU
+            if (m % 2 == 1)
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+            if (CP && C1 > C0 && m == 7)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (copy)
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (T == 2 || T == 6)
+            wait_vm<0>();  // the next group's codes (copied 3 stages ago) and scales
+        wait_lgkm0();      // (tells the compiler the barrier's wait happened)
+        lds_barrier();
+        // the codes stage s+1 decodes (stage s+2, visible since this
+        // barrier) and the first fragments of stage s+1
+        stage_codes(IntC<(T + 2) & 7>{});
+        read_frags(lds_f[CUR ^ 1], 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        if (CP && C2 > C1)
+            issue_group(G2, IntC<BUF>{}, IntC<C1>{}, IntC<C2>{});
+        if (CP && C2 - C1 == 3) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (copy)
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        } else if (CP && C2 - C1 == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+        } else if (CP && C2 - C1 == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // those reads have landed under the MFMAs: retire them so the next
+        // stage starts with an empty LDS counter and decodes without a wait
+        wait_lgkm0();
+        if (T == 7) {
+#pragma unroll
+            for (int i = 0; i < RPT; i++)
+                sc_cur[i] = sc_nxt[i];
+        }
+    };
+    // The loop body runs stages 3..10 mod 8: its back edge follows the wait
+    // at T == 2, where no copy is in flight, so the compiler's wait
+    // bookkeeping stays exact around the loop.
+    stage(0, IntC<0>{});
+    stage(1, IntC<1>{});
+    if (nst > 2)
+        stage(2, IntC<2>{});
+    wait_vm<0>();  // no-op after stage 2; keeps the wait bookkeeping exact on both paths
+    int64_t s = 3;
+    for (; s + 8 <= nst; s += 8) {
+        stage(s, IntC<3>{});
+        stage(s + 1, IntC<4>{});
+        stage(s + 2, IntC<5>{});
+        stage(s + 3, IntC<6>{});
+        stage(s + 4, IntC<7>{});
+        stage(s + 5, IntC<0>{});
+        stage(s + 6, IntC<1>{});
+        stage(s + 7, IntC<2>{});
+    }
+    if (s < nst)
+        stage(s, IntC<3>{});
+    if (s + 1 < nst)
+        stage(s + 1, IntC<4>{});
+    if (s + 2 < nst)
+        stage(s + 2, IntC<5>{});
+    if (s + 3 < nst)
+        stage(s + 3, IntC<6>{});
+    if (s + 4 < nst)
+        stage(s + 4, IntC<7>{});
+    if (s + 5 < nst)
+        stage(s + 5, IntC<0>{});
+    if (s + 6 < nst)
+        stage(s + 6, IntC<1>{});
+    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane);
 }
 
 }  // namespace nvfp4

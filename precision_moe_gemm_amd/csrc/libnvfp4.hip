@@ -116,6 +116,20 @@ nvfp4_status launch_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     return launch_status();
 }
 
+template <int BM, int BN, int MODE>
+nvfp4_status launch_tile(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
+{
+    p.m_tiles = m_tiles_ub;
+    int64_t blocks = m_tiles_ub * p.n_tiles;
+    if (blocks == 0)
+        return NVFP4_OK;
+    blocks = ceil_div(blocks, 8) * 8;
+    if (blocks > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    gemm_tile_kernel<BM, BN, MODE><<<(unsigned)blocks, 256, 0, st>>>(p);
+    return launch_status();
+}
+
 // The weight-streaming kernel serves A operands of at most 32 rows per
 // expert (on average; tiles of 16 rows) when K is a multiple of its
 // 256-element stage.
@@ -173,9 +187,9 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
     p.ksplit = 1;
     p.n_tiles = ceil_div(p.N, 256);
     if (p.M >= 256)
-        return launch_gemm<256, 256, 2, 2, kModeDense>(p, ceil_div(p.M, 256), st);
+        return launch_tile<256, 256, kModeDense>(p, ceil_div(p.M, 256), st);
     if (p.M >= 96)
-        return launch_gemm<128, 256, 2, 2, kModeDense>(p, ceil_div(p.M, 128), st);
+        return launch_tile<128, 256, kModeDense>(p, ceil_div(p.M, 128), st);
     if (p.M > 32)
         return launch_gemm<64, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 64), st);
     return launch_gemm<32, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 32), st);
@@ -236,7 +250,7 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
         GemmArgs q = cls(0);
         q.ksplit = 1;
         q.n_tiles = ceil_div(p.N, big_cols);
-        s = launch_gemm<256, 256, 2, 2, MODE>(q, total_rows / 128 + 1, st);
+        s = launch_tile<256, 256, MODE>(q, total_rows / 128 + 1, st);
         if (s != NVFP4_OK)
             return s;
     }
@@ -244,7 +258,7 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
         GemmArgs q = cls(1);
         q.ksplit = 1;
         q.n_tiles = ceil_div(p.N, big_cols);
-        s = launch_gemm<128, 256, 2, 2, MODE>(q, std::min<int64_t>(experts, total_rows / 65 + 1), st);
+        s = launch_tile<128, 256, MODE>(q, std::min<int64_t>(experts, total_rows / 65 + 1), st);
         if (s != NVFP4_OK)
             return s;
     }
