@@ -219,13 +219,24 @@ int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 // Streaming tile rows of a grouped projection with reduction length K.
 int grouped_small_bm(int64_t K) { return K % kSkBK == 0 ? kSkBM : 32; }
 
+// All rows of a grouped projection take 16-row weight-streaming tiles when
+// the down projection is K-split, or when the batch has at most 64 tokens:
+// top-k routing sends a token to an expert at most once, so no expert can
+// fill a 128- or 256-row tile and those launches would be empty.  (Any ids
+// still come out right: small tiles cover every row of every expert.)
+int grouped_all_small(int64_t T, int64_t K, int ksplit)
+{
+    if (K % kSkBK != 0)
+        return 0;
+    return (ksplit > 1 || T <= 64) ? 1 : 0;
+}
+
 template <int MODE>
 nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_rows, int experts,
-                              int32_t* plan, bool plan_ready, hipStream_t st)
+                              int all_small, int32_t* plan, bool plan_ready, hipStream_t st)
 {
     const bool stream_ok = p.K % kSkBK == 0;
     const int small_bm = grouped_small_bm(p.K);
-    const int all_small = p.ksplit > 1 ? 1 : 0;
     if (p.ksplit < 1 || !stream_ok || MODE != kModeDown)
         p.ksplit = 1;
     nvfp4_status s = NVFP4_OK;
@@ -263,10 +274,12 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
             return s;
     }
     GemmArgs q = cls(3);
-    // class 3: at most 4 tiles per expert (64 rows; 16 tiles with all_small,
-    // <= 256 rows), each holding at least one row
-    const int64_t m_small = std::min<int64_t>((int64_t)experts * (all_small ? ceil_div(256, kSkBM) : 4),
-                                              total_rows);
+    // class 3: every tile holds at least one row; at most 4 tiles per expert
+    // (64 rows) unless all rows take small tiles, then at most one partial
+    // tile per non-empty expert
+    const int64_t m_small =
+        all_small ? std::min<int64_t>(total_rows, total_rows / small_bm + std::min<int64_t>(experts, total_rows))
+                  : std::min<int64_t>((int64_t)experts * 4, total_rows);
     if (stream_ok) {
         q.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? kSkBN / 2 : kSkBN);
         return launch_stream_gemm<MODE>(q, m_small, st);
@@ -331,13 +344,13 @@ inline T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
 nvfp4_status route_impl(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
                         int32_t* offsets, int32_t* inv, void* ws, const RouteLayout& L,
                         uint32_t* zero_word, hipStream_t st, int32_t* plan_gu = nullptr,
-                        int small_bm_gu = 0, int32_t* plan_dn = nullptr, int small_bm_dn = 0,
-                        int all_small_dn = 0)
+                        int small_bm_gu = 0, int all_small_gu = 0, int32_t* plan_dn = nullptr,
+                        int small_bm_dn = 0, int all_small_dn = 0)
 {
     const int64_t np = T * k;
     if (np <= kRouteSmall) {
         route_small_kernel<<<1, 1024, 0, st>>>(ids, (int)np, E, offsets, perm, inv, zero_word, plan_gu,
-                                               small_bm_gu, plan_dn, small_bm_dn, all_small_dn);
+                                               small_bm_gu, all_small_gu, plan_dn, small_bm_dn, all_small_dn);
         return launch_status();
     }
     if (plan_gu || plan_dn)
@@ -652,7 +665,8 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     p.out = h;
     p.h_amax = h_amax;
     p.ksplit = 1;
-    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_gu), plan_ready, st);
+    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, grouped_all_small(T, H, 1),
+                                         at<int32_t>(ws, L.plan_gu), plan_ready, st);
 }
 
 nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
@@ -698,7 +712,8 @@ static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets
     p.out = y;
     p.ksplit = ksplit;
     p.partial = y;
-    return dispatch_grouped<kModeDown>(p, offsets, T * k, E, at<int32_t>(ws, L.plan_dn), plan_ready, st);
+    return dispatch_grouped<kModeDown>(p, offsets, T * k, E, grouped_all_small(T, I, ksplit),
+                                       at<int32_t>(ws, L.plan_dn), plan_ready, st);
 }
 
 nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
@@ -715,10 +730,10 @@ nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* 
         return NVFP4_ERR_SHAPE;
     if (T == 0 || H == 0)
         return NVFP4_OK;
-    if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 16))
+    if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 8))
         return NVFP4_ERR_INVALID_ARG;
-    combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, 1, 0,
-                                                                           (u32x4*)out);
+    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, 1, 0,
+                                                                           (u32x2*)out);
     return launch_status();
 }
 
@@ -753,8 +768,8 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     const bool small = T * k <= kRouteSmall;
     if (small)
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
-                       grouped_small_bm(H), at<int32_t>(ws, L.r.plan_dn), grouped_small_bm(I),
-                       ksplit > 1 ? 1 : 0);
+                       grouped_small_bm(H), grouped_all_small(T, H, 1), at<int32_t>(ws, L.r.plan_dn),
+                       grouped_small_bm(I), grouped_all_small(T, I, ksplit));
     else
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
     if (s != NVFP4_OK)
@@ -788,8 +803,8 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     // 6. combine (adds the planes of y in order)
     if (!w || H % 8 != 0)
         return NVFP4_ERR_SHAPE;
-    combine_kernel<<<stream_grid(T * (H / 8), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
-                                                                   (u32x4*)out);
+    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
+                                                                   (u32x2*)out);
     return launch_status();
 }
 

@@ -273,9 +273,10 @@ constexpr int kRouteSmall = 1024;
 __global__ void __launch_bounds__(1024)
 route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
                    int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
-                   int32_t* plan_gu, int small_bm_gu, int32_t* plan_dn, int small_bm_dn, int all_small_dn)
+                   int32_t* plan_gu, int small_bm_gu, int all_small_gu, int32_t* plan_dn, int small_bm_dn,
+                   int all_small_dn)
 {
-    __shared__ int32_t sid[kRouteSmall];
+    __shared__ __attribute__((aligned(16))) int32_t sid[kRouteSmall];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t lds16[16];
     const int tid = threadIdx.x;
@@ -320,8 +321,21 @@ route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* 
         if (my < 0) {
             inv[tid] = -1;
         } else {
+            // earlier pairs with the same id: 16 ids per step, four
+            // 16-byte LDS reads in flight
             int32_t rank = 0;
-            for (int i = 0; i < tid; i++)
+            const int4* s4 = (const int4*)sid;
+            const int full = tid >> 4;
+            for (int q = 0; q < full; q++) {
+                int4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    v[u] = s4[4 * q + u];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    rank += (v[u].x == my) + (v[u].y == my) + (v[u].z == my) + (v[u].w == my);
+            }
+            for (int i = full << 4; i < tid; i++)
                 rank += sid[i] == my;
             const int32_t q = off[my] + rank;
             perm[q] = tid;
@@ -329,41 +343,69 @@ route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* 
         }
     }
     if (plan_gu)
-        plan_block(off, E, small_bm_gu, 0, plan_gu, lds16);
+        plan_block(off, E, small_bm_gu, all_small_gu, plan_gu, lds16);
     if (plan_dn)
         plan_block(off, E, small_bm_dn, all_small_dn, plan_dn, lds16);
 }
 
-// out[t, 8c..8c+8) = bf16(sum_j w[t,j] * y[inv[t*k+j], 8c..8c+8)), where
-// y is the sum (in plane order) of `planes` partial planes `plane` floats apart
+// Sum over the `planes` partial planes (`plane` floats apart) of the four
+// floats at p, added in plane order; the loads of four planes are in flight
+// together.
+NVFP4_DEV float4_t sum_planes(const float* p, int planes, int64_t plane)
+{
+    float4_t v = *(const float4_t*)p;
+    for (int sp = 1; sp < planes; sp += 4) {
+        float4_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            x[u] = sp + u < planes ? *(const float4_t*)(p + (sp + u) * plane) : (float4_t){0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            if (sp + u < planes)
+                v += x[u];
+    }
+    return v;
+}
+
+// out[t, 4c..4c+4) = bf16(sum_j w[t,j] * y[inv[t*k+j], 4c..4c+4)), j in
+// ascending order, where y is the sum (in plane order) of `planes` partial
+// planes `plane` floats apart.  The rows of four consecutive j are fetched
+// together.
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
                const float* __restrict__ w, int64_t T, int k, int64_t H, int planes, int64_t plane,
-               u32x4* __restrict__ out)
+               u32x2* __restrict__ out)
 {
-    const int64_t groups = H / 8;
+    const int64_t groups = H / 4;
     const int64_t total = T * groups;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
         const int64_t t = i / groups, c = i - t * groups;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; j++) {
-            const int32_t q = inv[t * k + j];
-            if (q < 0)
-                continue;
-            const float wt = w[t * k + j];
-            const float4_t* src = (const float4_t*)(y + (int64_t)q * H + 8 * c);
-            float4_t v0 = src[0], v1 = src[1];
-            for (int sp = 1; sp < planes; sp++) {
-                const float4_t* ps = (const float4_t*)((const float*)src + sp * plane);
-                v0 += ps[0];
-                v1 += ps[1];
+        float4_t acc = {0, 0, 0, 0};
+        for (int j0 = 0; j0 < k; j0 += 4) {
+            int32_t q[4];
+            float wt[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const bool in = j0 + u < k;
+                q[u] = in ? inv[t * k + j0 + u] : -1;
+                wt[u] = in ? w[t * k + j0 + u] : 0.0f;
             }
-            acc[0] += wt * v0.x; acc[1] += wt * v0.y; acc[2] += wt * v0.z; acc[3] += wt * v0.w;
-            acc[4] += wt * v1.x; acc[5] += wt * v1.y; acc[6] += wt * v1.z; acc[7] += wt * v1.w;
+            float4_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                v[u] = q[u] >= 0 ? sum_planes(y + (int64_t)q[u] * H + 4 * c, planes, plane) : (float4_t){0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                if (q[u] >= 0) {
+                    acc.x += wt[u] * v[u].x;
+                    acc.y += wt[u] * v[u].y;
+                    acc.z += wt[u] * v[u].z;
+                    acc.w += wt[u] * v[u].w;
+                }
+            }
         }
-        out[i] = (u32x4){pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+        out[i] = (u32x2){pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
     }
 }
 
