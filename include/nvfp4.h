@@ -78,7 +78,18 @@ typedef struct {
     int64_t rows;
     int64_t cols;   /* multiple of 16 */
     int64_t batch;  /* >= 1 */
+    uint32_t flags; /* NVFP4_POW2_SCALES or 0 (see below) */
 } nvfp4_tensor;
+
+/* nvfp4_tensor.flags: every block scale is a power of two (or zero).  The
+ * library only reads it; the caller sets it on the output of
+ * mxfp4_to_nvfp4 (whose scales are 2^k or zero by construction) and clears
+ * it for tensors from nvfp4_quantize.  When a GEMM's weight operand carries
+ * it, the weight block scale is folded into the fp4 -> f16 conversion
+ * (which applies a power-of-two factor exactly) instead of a separate
+ * multiply; the product is the same.  Setting it on a tensor with other
+ * scales gives wrong results. */
+#define NVFP4_POW2_SCALES 1u
 
 /* Operations for nvfp4_workspace_size(). */
 enum {

@@ -68,6 +68,7 @@ class NVFP4Tensor:
     rows: int
     cols: int
     batch: int = 1
+    flags: int = 0  # _lib.POW2_SCALES when every block scale is a power of two
 
     @staticmethod
     def empty(rows: int, cols: int, batch: int = 1, device="cuda") -> "NVFP4Tensor":
@@ -79,7 +80,7 @@ class NVFP4Tensor:
 
     def c(self) -> _lib.NVFP4TensorC:
         return _lib.NVFP4TensorC(self.packed.data_ptr(), self.scales.data_ptr(),
-                                 self.global_.data_ptr(), self.rows, self.cols, self.batch)
+                                 self.global_.data_ptr(), self.rows, self.cols, self.batch, self.flags)
 
     @property
     def device(self):
@@ -118,6 +119,7 @@ def nvfp4_quantize(x: torch.Tensor, static_global: torch.Tensor | None = None,
                                    ctypes.byref(oc), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(x.device))
     _check(st, "nvfp4_quantize")
+    out.flags = 0
     return out
 
 
@@ -160,6 +162,7 @@ def mxfp4_to_nvfp4(packed: torch.Tensor, e8m0: torch.Tensor, rows: int, cols: in
     oc = out.c()
     _check(_lib.load().mxfp4_to_nvfp4(_ptr(packed), _ptr(e8m0), rows, cols, batch, ctypes.byref(oc),
                                       _ptr(ws), ws.numel(), _stream(dev)), "mxfp4_to_nvfp4")
+    out.flags = _lib.POW2_SCALES  # remapped scales are 2^k or zero
     return out
 
 

@@ -28,7 +28,11 @@ class NVFP4TensorC(ctypes.Structure):
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
         ("batch", ctypes.c_int64),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+POW2_SCALES = 1  # NVFP4_POW2_SCALES
 
 
 # name -> (restype, argtypes); mirrors include/nvfp4.h

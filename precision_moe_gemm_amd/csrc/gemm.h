@@ -69,6 +69,9 @@ struct GemmArgs {
     // (ksplit > 1 only; M = rows of the output)
     int32_t ksplit;
     float* partial;
+    // every W block scale is a power of two (or zero): the scale is folded
+    // into the fp4 -> f16 conversion
+    int32_t w_pow2;
 };
 
 // 16-byte chunk slot of chunk c in tile row r (8 chunks per row).
@@ -91,6 +94,18 @@ NVFP4_DEV u32x4 decode_chunk(uint32_t codes, _Float16 s)
     r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss);
     r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss);
     r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss);
+    return r;
+}
+
+// 8 codes times a power-of-two (or zero) scale s: the conversion applies
+// 2^exponent(s) exactly, so q * s needs no separate multiply.
+NVFP4_DEV u32x4 decode_chunk_p2(uint32_t codes, float s)
+{
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 3));
     return r;
 }
 
@@ -556,7 +571,7 @@ NVFP4_DEV void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int MODE, bool P2>
 __global__ void __launch_bounds__(256)
 gemm_tile_kernel(GemmArgs p)
 {
@@ -686,11 +701,21 @@ gemm_tile_kernel(GemmArgs p)
         for (int i = 0; i < RPT; i++) {
             const int r = drow[i];
             const uint32_t sw = (T >> 1) == 0 ? sc[i].x : (T >> 1) == 1 ? sc[i].y : (T >> 1) == 2 ? sc[i].z : sc[i].w;
-            const half2_t s2 = (T & 1) ? scales2<1>(sw) : scales2<0>(sw);
-            *(u32x4*)(dst + tpos(r, 0)) = decode_chunk(dcodes[i].x, s2.x);
-            *(u32x4*)(dst + tpos(r, 1)) = decode_chunk(dcodes[i].y, s2.x);
-            *(u32x4*)(dst + tpos(r, 2)) = decode_chunk(dcodes[i].z, s2.y);
-            *(u32x4*)(dst + tpos(r, 3)) = decode_chunk(dcodes[i].w, s2.y);
+            if (P2 && i * NT >= BM) {
+                // rows of this pass are all W rows: power-of-two scales
+                const float s0 = __builtin_amdgcn_cvt_f32_fp8(sw, 2 * (T & 1));
+                const float s1 = __builtin_amdgcn_cvt_f32_fp8(sw, 2 * (T & 1) + 1);
+                *(u32x4*)(dst + tpos(r, 0)) = decode_chunk_p2(dcodes[i].x, s0);
+                *(u32x4*)(dst + tpos(r, 1)) = decode_chunk_p2(dcodes[i].y, s0);
+                *(u32x4*)(dst + tpos(r, 2)) = decode_chunk_p2(dcodes[i].z, s1);
+                *(u32x4*)(dst + tpos(r, 3)) = decode_chunk_p2(dcodes[i].w, s1);
+            } else {
+                const half2_t s2 = (T & 1) ? scales2<1>(sw) : scales2<0>(sw);
+                *(u32x4*)(dst + tpos(r, 0)) = decode_chunk(dcodes[i].x, s2.x);
+                *(u32x4*)(dst + tpos(r, 1)) = decode_chunk(dcodes[i].y, s2.x);
+                *(u32x4*)(dst + tpos(r, 2)) = decode_chunk(dcodes[i].z, s2.y);
+                *(u32x4*)(dst + tpos(r, 3)) = decode_chunk(dcodes[i].w, s2.y);
+            }
         }
     };
 
@@ -901,7 +926,7 @@ NVFP4_DEV int sk_wslot(int r, int c) { return c ^ ((r >> 1) & 7); }
 // 16-byte slot of f16 chunk c (of 32) in A tile row r
 NVFP4_DEV int sk_aslot(int r, int c) { return c ^ (r & 15); }
 
-template <int MODE>
+template <int MODE, bool P2>
 __global__ void __launch_bounds__(kSkThreads)
 gemm_stream_kernel(GemmArgs p)
 {
@@ -1030,12 +1055,19 @@ gemm_stream_kernel(GemmArgs p)
         for (int q = 0; q < 2; q++) {
             u32x4 piece[2];
             half2_t s2[2];
+            float sf[2][2];
 #pragma unroll
             for (int f = 0; f < 2; f++) {
                 const int r = 32 * wave + 16 * f + fr;
                 piece[f] = *(const u32x4*)(&lds_w[b][r * 128 + 16 * sk_wslot(r, 4 * q + kg)]);
                 // blocks 8 q + 2 kg + {0, 1} of the stage
-                s2[f] = scales2<0>(*(const uint16_t*)(&lds_ws[b][r * 16 + 8 * q + 2 * kg]));
+                const uint32_t sb = *(const uint16_t*)(&lds_ws[b][r * 16 + 8 * q + 2 * kg]);
+                if (P2) {
+                    sf[f][0] = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
+                    sf[f][1] = __builtin_amdgcn_cvt_f32_fp8(sb, 1);
+                } else {
+                    s2[f] = scales2<0>(sb);
+                }
             }
 #pragma unroll
             for (int d = 0; d < 4; d++) {
@@ -1044,7 +1076,8 @@ gemm_stream_kernel(GemmArgs p)
                 for (int f = 0; f < 2; f++) {
                     const u32x4 pv = piece[f];
                     const uint32_t codes = d == 0 ? pv.x : d == 1 ? pv.y : d == 2 ? pv.z : pv.w;
-                    const u32x4 dv = decode_chunk(codes, d < 2 ? s2[f].x : s2[f].y);
+                    const u32x4 dv = P2 ? decode_chunk_p2(codes, sf[f][d >> 1])
+                                        : decode_chunk(codes, d < 2 ? s2[f].x : s2[f].y);
                     acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, __builtin_bit_cast(half8_t, dv),
                                                                     acc[f], 0, 0, 0);
                 }

@@ -126,7 +126,10 @@ nvfp4_status launch_tile(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     blocks = ceil_div(blocks, 8) * 8;
     if (blocks > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    gemm_tile_kernel<BM, BN, MODE><<<(unsigned)blocks, 256, 0, st>>>(p);
+    if (p.w_pow2)
+        gemm_tile_kernel<BM, BN, MODE, true><<<(unsigned)blocks, 256, 0, st>>>(p);
+    else
+        gemm_tile_kernel<BM, BN, MODE, false><<<(unsigned)blocks, 256, 0, st>>>(p);
     return launch_status();
 }
 
@@ -165,7 +168,10 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     blocks = ceil_div(blocks, 8) * 8;
     if (blocks > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    gemm_stream_kernel<MODE><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    if (p.w_pow2)
+        gemm_stream_kernel<MODE, true><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    else
+        gemm_stream_kernel<MODE, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
     nvfp4_status s = launch_status();
     if (s != NVFP4_OK || p.ksplit <= 1 || MODE != kModeDense)
         return s;  // grouped down: the combine adds the planes
@@ -569,6 +575,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
     p.w_packed = W->packed;
     p.w_scales = W->scales;
     p.w_global = W->global;
+    p.w_pow2 = (W->flags & NVFP4_POW2_SCALES) != 0;
     p.K = A->cols;
     p.M = A->rows;
     p.N = W->rows;
@@ -657,6 +664,7 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     p.w_packed = w13->packed;
     p.w_scales = w13->scales;
     p.w_global = w13->global;
+    p.w_pow2 = (w13->flags & NVFP4_POW2_SCALES) != 0;
     p.K = H;
     p.N = I;
     p.perm = perm;
@@ -704,6 +712,7 @@ static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets
     p.w_packed = w2->packed;
     p.w_scales = w2->scales;
     p.w_global = w2->global;
+    p.w_pow2 = (w2->flags & NVFP4_POW2_SCALES) != 0;
     p.K = I;
     p.N = H;
     p.M = T * k;

@@ -19,7 +19,7 @@ from . import synth
 
 
 def expert_view(t: NVFP4Tensor, e: int) -> NVFP4Tensor:
-    return NVFP4Tensor(t.packed[e:e + 1], t.scales[e:e + 1], t.global_[e:e + 1], t.rows, t.cols, 1)
+    return NVFP4Tensor(t.packed[e:e + 1], t.scales[e:e + 1], t.global_[e:e + 1], t.rows, t.cols, 1, t.flags)
 
 
 @dataclass

@@ -147,3 +147,28 @@ def test_gemm_deterministic():
     x, w = synth.C1.x(DEV), synth.C1.w(DEV)
     A, W = nv.nvfp4_quantize(x), nv.nvfp4_quantize(w)
     assert torch.equal(nv.nvfp4_gemm(A, W), nv.nvfp4_gemm(A, W))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 256, 1024), (200, 256, 1024), (300, 256, 576), (16, 512, 1024)])
+def test_pow2_weight_scales(orc, M, N, K):
+    """A remapped MXFP4 weight (every block scale a power of two) flagged
+    NVFP4_POW2_SCALES takes the conversion-folded scale path: the product
+    must equal the general path's bit for bit, and the oracle within the
+    GEMM bar.  Shapes cover the 256- and 128-row tiles (K with a partial
+    last group) and the weight-streaming kernel."""
+    step(f"gemm pow2 weight scales {M}x{N}x{K}")
+    x = synth.normal_bf16((M, K), 1.0, (810, M, K))
+    w = synth.normal_bf16((N, K), 0.02, (811, N, K))
+    A = _q(x)
+    p, e = nv.mxfp4_quantize(w.to(DEV))
+    W = nv.mxfp4_to_nvfp4(p, e, N, K, 1)
+    assert W.flags == nv._lib.POW2_SCALES
+    Wg = nv.NVFP4Tensor(W.packed, W.scales, W.global_, N, K, 1, 0)
+    C = nv.nvfp4_gemm(A, W)
+    Cg = nv.nvfp4_gemm(A, Wg)
+    assert torch.equal(C, Cg)
+    Ao = orc.quantize(synth.bits(x))
+    Wo = orc.mxfp4_to_nvfp4(*orc.mxfp4_encode(synth.bits(w)))
+    err = rel_err(C.cpu().numpy(), orc.gemm(Ao, Wo))
+    print(f"pow2 scales rel err {err:.3e}")
+    assert err <= GEMM_TOL
