@@ -1116,7 +1116,21 @@ gemm_stream_kernel(GemmArgs p)
     // fragment ------------------------------------------------------------
     const float gscale = *p.a_global * p.w_global[e];
     const int rows_left = (int)(row_end - row_begin);
-    if (MODE == kModeGateUp) {
+    if (MODE == kModeGateUp && p.ksplit > 1) {
+        // K split: scaled partial gate and up sums to plane ks, rows of 2N
+        // (gate columns, then up columns); swiglu_reduce_kernel finishes
+        const int64_t col = nt * (BN / 2) + 16 * wave + fr;
+        float* part = p.partial + (int64_t)ks * p.M * 2 * p.N;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = 4 * kg + i;
+            if (m < rows_left) {
+                const int64_t o = (row_begin + m) * 2 * p.N + col;
+                part[o] = acc[0][i] * gscale;
+                part[o + p.N] = acc[1][i] * gscale;
+            }
+        }
+    } else if (MODE == kModeGateUp) {
         const int64_t col = nt * (BN / 2) + 16 * wave + fr;
         uint16_t* h = (uint16_t*)p.out + row_begin * p.N + col;
         uint32_t hmax = 0;
@@ -1160,6 +1174,35 @@ gemm_stream_kernel(GemmArgs p)
             }
         }
     }
+}
+
+// K-split gate_up: h[r, c] = bf16(silu(g) * u) with g, u the sums in split
+// order of the scaled partials (plane s: rows of 2N floats, gate then up);
+// max |h| to the atomic word as the unsplit epilogue does.
+__global__ void __launch_bounds__(256)
+swiglu_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t rows, int64_t N,
+                     uint16_t* __restrict__ h, uint32_t* h_amax)
+{
+    const int64_t count = rows * N;
+    const int64_t plane = rows * 2 * N;
+    uint32_t hmax = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / N, c = i - r * N;
+        const float* g = partial + r * 2 * N + c;
+        float gg = g[0], uu = g[N];
+        for (int s = 1; s < ksplit; s++) {
+            gg += g[(int64_t)s * plane];
+            uu += g[(int64_t)s * plane + N];
+        }
+        const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+        h[i] = hb;
+        const uint32_t mag = hb & 0x7FFFu;
+        hmax = hmax > mag ? hmax : mag;
+    }
+    hmax = wave_max_u32(hmax);
+    if ((threadIdx.x & 63) == 0 && hmax != 0)
+        atomicMax(h_amax, hmax << 16);
 }
 
 // Sum the scaled K-split partials in split order and store fp32 or bf16.

@@ -173,8 +173,14 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     else
         gemm_stream_kernel<MODE, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
     nvfp4_status s = launch_status();
-    if (s != NVFP4_OK || p.ksplit <= 1 || MODE != kModeDense)
+    if (s != NVFP4_OK || p.ksplit <= 1 || MODE == kModeDown)
         return s;  // grouped down: the combine adds the planes
+    if (MODE == kModeGateUp) {
+        const int64_t cnt = p.M * p.N;
+        const unsigned rb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(2048, ceil_div(cnt, 256)));
+        swiglu_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, p.M, p.N, (uint16_t*)p.out, p.h_amax);
+        return launch_status();
+    }
     const int64_t count = p.M * p.N;
     const unsigned rb = (unsigned)std::min<int64_t>(2048, ceil_div(count, 256));
     splitk_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, count, p.out, p.out_bf16);
@@ -205,17 +211,40 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
 // a one-expert layer, or a handful of tokens over few experts): every tile is
 // a 16-row weight-streaming tile and split s writes its scaled partial sums
 // to plane s of y, which the combine adds in split order.
+// Upper bound of the 16-row tiles the np pairs of a small batch fill: np/16
+// full tiles plus at most one partial tile per other non-empty expert.
+int64_t small_tiles_est(int64_t np, int32_t E) { return std::min<int64_t>(np, ceil_div(np, kSkBM) + E - 1); }
+
 int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 {
     const int64_t np = T * k;
     if (np <= 0 || np > 256 || I % kSkBK != 0)
         return 1;
-    const int64_t tiles = std::min<int64_t>(E, ceil_div(np, kSkBM)) * ceil_div(H, kSkBN);
+    const int64_t tiles = small_tiles_est(np, E) * ceil_div(H, kSkBN);
     if (tiles >= 512)
         return 1;
     int64_t s = 768 / tiles;
     s = std::min<int64_t>(s, I / kSkBK / 4);
     s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * H * 4));
+    return (int)std::max<int64_t>(1, s);
+}
+
+// K split of the fused gate_up projection of a tiny batch (as the down
+// projection): when the 16-row tiles cannot fill the chip, split s writes
+// scaled partial gate and up sums to plane s and swiglu_reduce_kernel adds
+// the planes in order before the SwiGLU.  One wave of workgroups at most
+// (3 per CU), at least four 256-element stages per split.
+int moe_gate_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
+{
+    const int64_t np = T * k;
+    if (np <= 0 || np > 256 || H % kSkBK != 0)
+        return 1;
+    const int64_t tiles = small_tiles_est(np, E) * ceil_div(I, kSkBN / 2);
+    if (tiles >= 512)
+        return 1;
+    int64_t s = 768 / tiles;
+    s = std::min<int64_t>(s, H / kSkBK / 4);
+    s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * 2 * I * 4));
     return (int)std::max<int64_t>(1, s);
 }
 
@@ -243,8 +272,10 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
 {
     const bool stream_ok = p.K % kSkBK == 0;
     const int small_bm = grouped_small_bm(p.K);
-    if (p.ksplit < 1 || !stream_ok || MODE != kModeDown)
+    if (p.ksplit < 1 || !stream_ok)
         p.ksplit = 1;
+    if (p.ksplit > 1)
+        all_small = 1;  // the split planes cover every row
     nvfp4_status s = NVFP4_OK;
     if (!plan_ready) {
         moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
@@ -317,7 +348,7 @@ RouteLayout route_layout(int64_t npairs, int32_t E)
 
 struct MoeLayout {
     RouteLayout r;
-    size_t perm, inv, xparts, xq_p, xq_s, gx, h, hmax, hq_p, hq_s, gh, y, end;
+    size_t perm, inv, xparts, xq_p, xq_s, gx, gpart, h, hmax, hq_p, hq_s, gh, y, end;
 };
 
 MoeLayout moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
@@ -332,6 +363,8 @@ MoeLayout moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
     L.xq_p = o; o = align256(o + (size_t)(T * H / 2));
     L.xq_s = o; o = align256(o + (size_t)(T * H / 16));
     L.gx = o; o = align256(o + sizeof(float));
+    const int gs = moe_gate_ksplit(T, k, E, H, I);
+    L.gpart = o; o = align256(o + (gs > 1 ? sizeof(float) * (size_t)(np * 2 * I) * gs : 0));
     L.h = o; o = align256(o + sizeof(uint16_t) * (size_t)(np * I));
     L.hmax = o; o = align256(o + sizeof(uint32_t));
     L.hq_p = o; o = align256(o + (size_t)(np * I / 2));
@@ -638,7 +671,7 @@ static nvfp4_status check_experts(const nvfp4_tensor* w13, const nvfp4_tensor* w
 static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
                                      int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
                                      uint32_t* h_amax, void* ws, size_t ws_bytes, bool plan_ready,
-                                     hipStream_t st)
+                                     hipStream_t st, int ksplit = 1, float* gpart = nullptr)
 {
     int64_t H = 0, I = 0;
     nvfp4_status s = check_experts(w13, nullptr, E, &H, &I);
@@ -672,8 +705,10 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     p.experts = E;
     p.out = h;
     p.h_amax = h_amax;
-    p.ksplit = 1;
-    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, grouped_all_small(T, H, 1),
+    p.M = T * k;
+    p.ksplit = gpart ? ksplit : 1;
+    p.partial = gpart;
+    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, grouped_all_small(T, H, p.ksplit),
                                          at<int32_t>(ws, L.plan_gu), plan_ready, st);
 }
 
@@ -774,10 +809,11 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     // 1. route (also zeroes the h max word); a small batch routes in one
     // workgroup that also plans both projections' tiles
     const int ksplit = moe_down_ksplit(T, k, E, H, I);
+    const int gsplit = moe_gate_ksplit(T, k, E, H, I);
     const bool small = T * k <= kRouteSmall;
     if (small)
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
-                       grouped_small_bm(H), grouped_all_small(T, H, 1), at<int32_t>(ws, L.r.plan_dn),
+                       grouped_small_bm(H), grouped_all_small(T, H, gsplit), at<int32_t>(ws, L.r.plan_dn),
                        grouped_small_bm(I), grouped_all_small(T, I, ksplit));
     else
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
@@ -793,7 +829,8 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         return s;
     // 3. gate_up + SwiGLU
     void* h = at<void>(ws, L.h);
-    s = moe_gate_up_impl(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, small, st);
+    s = moe_gate_up_impl(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, small, st, gsplit,
+                         gsplit > 1 ? at<float>(ws, L.gpart) : nullptr);
     if (s != NVFP4_OK)
         return s;
     // 4. quantize h over all T*k rows

@@ -183,6 +183,14 @@ def test_fused_down_k_split_small(orc):
     _check_moe(orc, cfg, fused_exact=False)
 
 
+def test_fused_gate_up_k_split_small(orc):
+    """12 tokens over 2 experts with H = 2048: the fused layer splits the
+    gate_up projection's K over two streaming workgroups (partial gate and
+    up planes, SwiGLU after the ordered sum)."""
+    cfg = synth.MoE(seed=37, E=2, k=1, H=2048, I=512, T=12)
+    _check_moe(orc, cfg, fused_exact=False)
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_dense_mlp_as_one_expert_sampled(orc, T):
     """The 27B-class MLP (H=5120, I=17408) as a one-expert layer at decode
