@@ -194,7 +194,8 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
  *      g || u = xq[t] W13[e]^T (W13[e] is [2I, H]: rows [0, I) gate (w1),
  *      rows [I, 2I) up (w3)), h = silu(g) * u rounded to bf16;
  *   4. quantize h over all T*k rows (dynamic G_h = amax(h)/2688, or
- *      static_in_globals[1]);
+ *      static_in_globals[1]: then step 3's epilogue encodes h to NVFP4
+ *      directly, as nvfp4_moe_gate_up_q, with the same bytes);
  *   5. down: y = hq W2[e]^T (W2[e] is [H, I]), fp32;
  *   6. combine: out[t] = sum_j topk_w[t, j] * y[t, j] (j in order, fp32),
  *      rounded to bf16.
@@ -235,6 +236,23 @@ nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm,
                                const int32_t* offsets, int64_t T, int32_t k, int32_t E,
                                const nvfp4_tensor* w13, void* h_bf16, uint32_t* h_amax,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gate_up + SwiGLU with the NVFP4 encode of h fused into the epilogue, for a
+ * calibrated (static) activation global G_h, as the checkpoints' per-layer
+ * input scales allow (page "Qwen3.8-Flash-Next-NVFP4", section 核心: static
+ * activation scales calibrated from the max; page "Qwen3.8-27B-NVFP4",
+ * section 2: input_scale in the checkpoint).  hq receives the bytes that
+ * nvfp4_quantize(h, static_global = h_global) would give for the h of
+ * nvfp4_moe_gate_up: codes [T*k, I/2] and scales [T*k, I/16] in list
+ * order; no bf16 h is written and no max is taken.  h_global: device
+ * float[1]; hq: rows T*k, cols I, batch 1 (hq->global is not written; point
+ * it at h_global for nvfp4_moe_down).  ws: as nvfp4_moe_route.
+ */
+nvfp4_status nvfp4_moe_gate_up_q(const nvfp4_tensor* xq, const int32_t* perm,
+                                 const int32_t* offsets, int64_t T, int32_t k, int32_t E,
+                                 const nvfp4_tensor* w13, const float* h_global,
+                                 const nvfp4_tensor* hq, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * down projection for every listed pair: y[q] = hq[q] W2[e]^T (fp32

@@ -21,7 +21,7 @@ from . import _lib
 __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
-    "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_down", "nvfp4_moe_combine",
+    "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
     "nvfp4_recipe", "status_string",
 ]
@@ -232,6 +232,28 @@ def nvfp4_moe_gate_up(xq: NVFP4Tensor, perm: torch.Tensor, offsets: torch.Tensor
                                          ctypes.byref(wc), _ptr(h), _ptr(hmax), _ptr(ws), ws.numel(),
                                          _stream(dev)), "nvfp4_moe_gate_up")
     return h, hmax
+
+
+def nvfp4_moe_gate_up_q(xq: NVFP4Tensor, perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                        w13: NVFP4Tensor, h_global: torch.Tensor, ws: torch.Tensor | None = None) -> NVFP4Tensor:
+    """gate_up + SwiGLU with h encoded to NVFP4 in the epilogue under the
+    static global h_global (float32 [1] on the device): the NVFP4 h [T*k, I]
+    (list order) whose global is h_global."""
+    T = xq.rows
+    E = w13.batch
+    I = w13.rows // 2
+    dev = xq.device
+    _need_cuda(h_global)
+    hq = NVFP4Tensor(torch.empty((1, T * k, I // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((1, T * k, I // 16), dtype=torch.uint8, device=dev),
+                     h_global.reshape(1), T * k, I, 1)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE_ROUTE, T, k, E), dev)
+    xc, wc, hc = xq.c(), w13.c(), hq.c()
+    _check(_lib.load().nvfp4_moe_gate_up_q(ctypes.byref(xc), _ptr(perm), _ptr(offsets), T, k, E,
+                                           ctypes.byref(wc), _ptr(h_global), ctypes.byref(hc), _ptr(ws),
+                                           ws.numel(), _stream(dev)), "nvfp4_moe_gate_up_q")
+    return hq
 
 
 def nvfp4_moe_down(hq: NVFP4Tensor, offsets: torch.Tensor, T: int, k: int, w2: NVFP4Tensor,

@@ -52,6 +52,7 @@ SIGNATURES = {
     "nvfp4_moe_grouped_gemm": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, P, SZ, P]),
     "nvfp4_moe_route": (ST, [P, I64, I32, I32, P, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up": (ST, [TP, P, P, I64, I32, I32, TP, P, P, P, SZ, P]),
+    "nvfp4_moe_gate_up_q": (ST, [TP, P, P, I64, I32, I32, TP, P, TP, P, SZ, P]),
     "nvfp4_moe_down": (ST, [TP, P, I64, I32, I32, TP, P, P, SZ, P]),
     "nvfp4_moe_combine": (ST, [P, P, P, I64, I32, I64, P, P]),
     "nvfp4_kv_quant": (ST, [P, P, I64, I64, I64, TP, TP, P]),

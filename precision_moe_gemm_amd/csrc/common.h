@@ -101,6 +101,81 @@ NVFP4_DEV float e4m3_decode(uint32_t c)
 // byte `sel` of `src` (two E2M1 codes) -> two f32 values (exact).
 #define FP4_TO_F32X2(src, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((src), 1.0f, (sel))
 
+// Scale of one 16-element block from its bf16 magnitude bits `am` (the
+// block amax): *sc gets the E4M3 byte, the return value is the reciprocal
+// r = 1 / (s * G) the codes are taken with (0 when s = 0).
+NVFP4_DEV float block_scale(uint32_t am, float G, float six_g, uint32_t* sc)
+{
+    const float ab = __uint_as_float(am << 16);
+    const float s_real = ab / six_g;
+    *sc = e4m3_encode(s_real);
+    const float s = e4m3_decode(*sc);
+    float r = 0.0f;                       // scale 0: every code becomes +-0
+    if (*sc != 0) {
+        const float p = s * G;
+        r = 1.0f / p;
+    }
+    return r;
+}
+
+// Eight bf16 values (one u32x4) times r -> eight E2M1 codes (one dword,
+// element 2j in the low nibble of byte j).
+NVFP4_DEV uint32_t encode_half(u32x4 v, float r)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        y[2 * i] = bf16_lo(w[i]) * r;
+        y[2 * i + 1] = bf16_hi(w[i]) * r;
+    }
+    if (__builtin_isinf(r)) {
+        // s * G underflowed: x * inf is +-inf (code 6) except 0 * inf, which
+        // is taken as a zero code with the sign of x.
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+            y[2 * i] = a == 0.0f ? a : y[2 * i];
+            y[2 * i + 1] = b == 0.0f ? b : y[2 * i + 1];
+        }
+    }
+    uint32_t c = 0;
+    c = FP4_PACK2(c, y[0], y[1], 0);
+    c = FP4_PACK2(c, y[2], y[3], 1);
+    c = FP4_PACK2(c, y[4], y[5], 2);
+    c = FP4_PACK2(c, y[6], y[7], 3);
+    return c;
+}
+
+// One NVFP4 block held by 16 consecutive lanes (lane 16 q + p holds
+// element p, as bf16 bits in the low half of hb), encoded as nvfp4_quantize
+// encodes it: the block max over the 16 lanes, block_scale, codes of x * r
+// (with the same zero rule for an infinite r).  Every lane gets the scale
+// byte; lanes with p = 0 and p = 8 get the dword of codes of elements
+// [0, 8) and [8, 16).  All 64 lanes must execute it.
+NVFP4_DEV void encode_block16(uint32_t hb, float G, float six_g, uint32_t* sc, uint32_t* codes)
+{
+    uint32_t am = hb & 0x7FFFu;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)am, off, 64);
+        am = am > o ? am : o;
+    }
+    const float r = block_scale(am, G, six_g, sc);
+    const float x = __uint_as_float(hb << 16);
+    float y = x * r;
+    if (__builtin_isinf(r) && x == 0.0f)
+        y = x;
+    const float yo = __shfl_xor(y, 1, 64);
+    const int p = threadIdx.x & 15;
+    // even lanes: elements p (low nibble) and p + 1 of byte p / 2
+    const uint32_t b = FP4_PACK2(0u, y, yo, 0) & 0xFFu;
+    uint32_t w = b << (8 * ((p >> 1) & 3));
+    w |= (uint32_t)__shfl_xor((int)w, 2, 64);
+    w |= (uint32_t)__shfl_xor((int)w, 4, 64);
+    *codes = w;
+}
+
 // ------------------------------------------------------------ reductions --
 
 NVFP4_DEV uint32_t wave_max_u32(uint32_t v)

@@ -72,6 +72,12 @@ struct GemmArgs {
     // every W block scale is a power of two (or zero): the scale is folded
     // into the fp4 -> f16 conversion
     int32_t w_pow2;
+    // gate_up with a static G_h (non-null): h is encoded to NVFP4 in the
+    // epilogue (codes [rows, N/2], scale bytes [rows, N/16]) instead of being
+    // written as bf16 with its max
+    const float* hq_global;
+    uint8_t* hq_packed;
+    uint8_t* hq_scales;
 };
 
 // 16-byte chunk slot of chunk c in tile row r (8 chunks per row).
@@ -207,7 +213,7 @@ NVFP4_DEV int64_t tile_w_row(const GemmArgs& p, const TileCoord& tc, int r)
 // rows (i % 4) + 8 (i / 4) + 4 (lane / 32) of each fragment.
 template <int BN, int WM, int WN, int TM, int TN, int FM, int FN, int MODE>
 NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&acc)[FM][FN], int wave_m,
-                          int wave_n, int lane)
+                          int wave_n, int lane, uint8_t* lds)
 {
     const float gscale = *p.a_global * p.w_global[tc.e];
     const int ncol = lane & 31;
@@ -215,7 +221,45 @@ NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&ac
     const int64_t wrow0 = tc.row_begin + wave_m * TM;  // first output row of this wave
     const int rows_left = (int)(tc.row_end - wrow0);
     const int ld = (int)p.N;
-    if (MODE == kModeGateUp) {
+    if (MODE == kModeGateUp && p.hq_global) {
+        // h straight to NVFP4 through LDS (free once the mainloop is done):
+        // the tile's bf16 h [BM, BN/2] goes to LDS, then each thread encodes
+        // whole 16-element blocks as the quantize kernel does
+        constexpr int HC = BN / 2;  // h columns of the tile
+        uint16_t* hs = (uint16_t*)lds;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int rr = wave_m * TM + i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
+#pragma unroll
+                for (int j = 0; j < FN / 2; j++) {
+                    const float gg = acc[i][j][r] * gscale;
+                    const float uu = acc[i][j + FN / 2][r] * gscale;
+                    hs[rr * HC + wave_n * (TN / 2) + j * 32 + ncol] = f32_to_bf16(silu_f(gg) * uu);
+                }
+            }
+        }
+        __syncthreads();
+        const float Gh = *p.hq_global, six = 6.0f * Gh;
+        const int64_t hcol0 = tc.nt * HC;
+        for (int b = threadIdx.x; b < WM * TM * (HC / 16); b += blockDim.x) {
+            const int row = b / (HC / 16), bc = b - row * (HC / 16);
+            const int64_t grow = tc.row_begin + row;
+            if (grow < tc.row_end) {
+                const u32x4 v0 = *(const u32x4*)(hs + row * HC + 16 * bc);
+                const u32x4 v1 = *(const u32x4*)(hs + row * HC + 16 * bc + 8);
+                const uint32_t a0 = absmax_bits8(v0), a1 = absmax_bits8(v1);
+                uint32_t sc;
+                const float rcp = block_scale(a0 > a1 ? a0 : a1, Gh, six, &sc);
+                const int64_t col = hcol0 + 16 * bc;
+                *(u32x2*)(p.hq_packed + grow * (p.N / 2) + col / 2) =
+                    (u32x2){encode_half(v0, rcp), encode_half(v1, rcp)};
+                p.hq_scales[grow * (p.N / 16) + col / 16] = (uint8_t)sc;
+            }
+        }
+    } else if (MODE == kModeGateUp) {
         const int64_t col0 = tc.nt * (BN / 2) + wave_n * (TN / 2) + ncol;
         uint16_t* h = (uint16_t*)p.out + wrow0 * p.N + col0;
         uint32_t hmax = 0;
@@ -515,7 +559,7 @@ gemm_kernel(GemmArgs p)
     if (s + 2 < nstages)
         stage(s + 2, IntC<2>{});
 
-    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane);
+    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane, &lds_w[0][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -887,7 +931,7 @@ gemm_tile_kernel(GemmArgs p)
         stage(s + 5, IntC<0>{});
     if (s + 6 < nst)
         stage(s + 6, IntC<1>{});
-    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane);
+    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane, &lds_f[0][0]);
 }
 
 }  // namespace nvfp4
@@ -1130,6 +1174,27 @@ gemm_stream_kernel(GemmArgs p)
                 part[o + p.N] = acc[1][i] * gscale;
             }
         }
+    } else if (MODE == kModeGateUp && p.hq_global) {
+        // h straight to NVFP4: the 16 lanes of a k-group hold the 16
+        // columns of one block of row 4 kg + i
+        const int64_t col = nt * (BN / 2) + 16 * wave + fr;
+        const float Gh = *p.hq_global, six = 6.0f * Gh;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = 4 * kg + i;
+            const float gg = acc[0][i] * gscale;
+            const float uu = acc[1][i] * gscale;
+            const uint32_t hb = f32_to_bf16(silu_f(gg) * uu);
+            uint32_t sc, codes;
+            encode_block16(hb, Gh, six, &sc, &codes);
+            if (m < rows_left) {
+                const int64_t row = row_begin + m;
+                if ((fr & 7) == 0)
+                    *(uint32_t*)(p.hq_packed + row * (p.N / 2) + (col >> 1)) = codes;
+                if (fr == 0)
+                    p.hq_scales[row * (p.N / 16) + (col >> 4)] = (uint8_t)sc;
+            }
+        }
     } else if (MODE == kModeGateUp) {
         const int64_t col = nt * (BN / 2) + 16 * wave + fr;
         uint16_t* h = (uint16_t*)p.out + row_begin * p.N + col;
@@ -1179,12 +1244,16 @@ gemm_stream_kernel(GemmArgs p)
 // K-split gate_up: h[r, c] = bf16(silu(g) * u) with g, u the sums in split
 // order of the scaled partials (plane s: rows of 2N floats, gate then up);
 // max |h| to the atomic word as the unsplit epilogue does.
+// With a static G_h (hq_global non-null) h is encoded to NVFP4 instead:
+// 16 consecutive threads hold one block (N % 16 == 0).
 __global__ void __launch_bounds__(256)
 swiglu_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t rows, int64_t N,
-                     uint16_t* __restrict__ h, uint32_t* h_amax)
+                     uint16_t* __restrict__ h, uint32_t* h_amax, const float* hq_global,
+                     uint8_t* __restrict__ hq_packed, uint8_t* __restrict__ hq_scales)
 {
     const int64_t count = rows * N;
     const int64_t plane = rows * 2 * N;
+    const float Gh = hq_global ? *hq_global : 1.0f, six = 6.0f * Gh;
     uint32_t hmax = 0;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -1196,6 +1265,15 @@ swiglu_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t rows
             uu += g[(int64_t)s * plane + N];
         }
         const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+        if (hq_global) {
+            uint32_t sc, codes;
+            encode_block16(hb, Gh, six, &sc, &codes);
+            if ((i & 7) == 0)
+                *(uint32_t*)(hq_packed + (i >> 1)) = codes;
+            if ((i & 15) == 0)
+                hq_scales[i >> 4] = (uint8_t)sc;
+            continue;
+        }
         h[i] = hb;
         const uint32_t mag = hb & 0x7FFFu;
         hmax = hmax > mag ? hmax : mag;

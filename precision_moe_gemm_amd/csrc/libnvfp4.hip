@@ -178,7 +178,8 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     if (MODE == kModeGateUp) {
         const int64_t cnt = p.M * p.N;
         const unsigned rb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(2048, ceil_div(cnt, 256)));
-        swiglu_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, p.M, p.N, (uint16_t*)p.out, p.h_amax);
+        swiglu_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, p.M, p.N, (uint16_t*)p.out, p.h_amax,
+                                                 p.hq_global, p.hq_packed, p.hq_scales);
         return launch_status();
     }
     const int64_t count = p.M * p.N;
@@ -671,7 +672,8 @@ static nvfp4_status check_experts(const nvfp4_tensor* w13, const nvfp4_tensor* w
 static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
                                      int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
                                      uint32_t* h_amax, void* ws, size_t ws_bytes, bool plan_ready,
-                                     hipStream_t st, int ksplit = 1, float* gpart = nullptr)
+                                     hipStream_t st, int ksplit = 1, float* gpart = nullptr,
+                                     const float* hq_global = nullptr, const nvfp4_tensor* hq = nullptr)
 {
     int64_t H = 0, I = 0;
     nvfp4_status s = check_experts(w13, nullptr, E, &H, &I);
@@ -679,8 +681,15 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
         s = check_tensor(xq);
     if (s != NVFP4_OK)
         return s;
-    if (!perm || !offsets || !h || !h_amax || !ws || !aligned(ws, 256))
+    if (!perm || !offsets || !ws || !aligned(ws, 256))
         return NVFP4_ERR_INVALID_ARG;
+    if (hq_global) {
+        // h encoded in the epilogue: hq rows are list positions
+        if (!hq || !hq->packed || !hq->scales || !aligned(hq_global, 4) || !aligned(hq->packed, 4))
+            return NVFP4_ERR_INVALID_ARG;
+    } else if (!h || !h_amax) {
+        return NVFP4_ERR_INVALID_ARG;
+    }
     if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || xq->rows != T || xq->cols != H || xq->batch != 1)
         return NVFP4_ERR_SHAPE;
     if (H % kBK != 0 || I % 128 != 0)
@@ -703,8 +712,13 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     p.perm = perm;
     p.topk = k;
     p.experts = E;
+    if (hq_global && (hq->rows != T * k || hq->cols != I || hq->batch != 1))
+        return NVFP4_ERR_SHAPE;
     p.out = h;
     p.h_amax = h_amax;
+    p.hq_global = hq_global;
+    p.hq_packed = hq_global ? hq->packed : nullptr;
+    p.hq_scales = hq_global ? hq->scales : nullptr;
     p.M = T * k;
     p.ksplit = gpart ? ksplit : 1;
     p.partial = gpart;
@@ -717,6 +731,17 @@ nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, cons
                                uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream)
 {
     return moe_gate_up_impl(xq, perm, offsets, T, k, E, w13, h, h_amax, ws, ws_bytes, false, S(stream));
+}
+
+nvfp4_status nvfp4_moe_gate_up_q(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+                                 int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13,
+                                 const float* h_global, const nvfp4_tensor* hq, void* ws, size_t ws_bytes,
+                                 void* stream)
+{
+    if (!h_global)
+        return NVFP4_ERR_INVALID_ARG;
+    return moe_gate_up_impl(xq, perm, offsets, T, k, E, w13, nullptr, nullptr, ws, ws_bytes, false, S(stream),
+                            1, nullptr, h_global, hq);
 }
 
 static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
@@ -827,20 +852,23 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         s = quantize_impl(x, T, H, H, kGlobalPartials, nullptr, &xq, 0, at<uint32_t>(ws, L.xparts), st);
     if (s != NVFP4_OK)
         return s;
-    // 3. gate_up + SwiGLU
+    // 3. gate_up + SwiGLU; with a static G_h the epilogue encodes h to NVFP4
+    // directly (no bf16 h, no max, no separate quantize)
     void* h = at<void>(ws, L.h);
-    s = moe_gate_up_impl(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, small, st, gsplit,
-                         gsplit > 1 ? at<float>(ws, L.gpart) : nullptr);
-    if (s != NVFP4_OK)
-        return s;
-    // 4. quantize h over all T*k rows
     nvfp4_tensor hq{at<uint8_t>(ws, L.hq_p), at<uint8_t>(ws, L.hq_s), at<float>(ws, L.gh), T * k, I, 1};
     if (static_in_globals)
-        s = quantize_impl(h, T * k, I, I, kGlobalStatic, static_in_globals + 1, &hq, 0, nullptr, st);
-    else
-        s = quantize_impl(h, T * k, I, I, kGlobalAmaxWord, hmax, &hq, 0, nullptr, st);
+        hq.global = (float*)(static_in_globals + 1);
+    s = moe_gate_up_impl(&xq, perm, offsets, T, k, E, w13, h, hmax, ws, L.r.end, small, st, gsplit,
+                         gsplit > 1 ? at<float>(ws, L.gpart) : nullptr,
+                         static_in_globals ? static_in_globals + 1 : nullptr, &hq);
     if (s != NVFP4_OK)
         return s;
+    // 4. quantize h over all T*k rows (dynamic G_h from the max word)
+    if (!static_in_globals) {
+        s = quantize_impl(h, T * k, I, I, kGlobalAmaxWord, hmax, &hq, 0, nullptr, st);
+        if (s != NVFP4_OK)
+            return s;
+    }
     // 5. down (K split into planes of y for tiny batches)
     float* y = at<float>(ws, L.y);
     s = moe_down_impl(&hq, offsets, T, k, E, w2, y, ksplit, ws, L.r.end, small, st);

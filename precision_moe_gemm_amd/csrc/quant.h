@@ -66,52 +66,6 @@ NVFP4_DEV float load_global(int src, const void* gsrc, int nparts, uint32_t* lds
     return global_from_amax(__uint_as_float(m));
 }
 
-// Scale of one 16-element block from its bf16 magnitude bits `am` (the
-// block amax): *sc gets the E4M3 byte, the return value is the reciprocal
-// r = 1 / (s * G) the codes are taken with (0 when s = 0).
-NVFP4_DEV float block_scale(uint32_t am, float G, float six_g, uint32_t* sc)
-{
-    const float ab = __uint_as_float(am << 16);
-    const float s_real = ab / six_g;
-    *sc = e4m3_encode(s_real);
-    const float s = e4m3_decode(*sc);
-    float r = 0.0f;                       // scale 0: every code becomes +-0
-    if (*sc != 0) {
-        const float p = s * G;
-        r = 1.0f / p;
-    }
-    return r;
-}
-
-// Eight bf16 values (one u32x4) times r -> eight E2M1 codes (one dword,
-// element 2j in the low nibble of byte j).
-NVFP4_DEV uint32_t encode_half(u32x4 v, float r)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        y[2 * i] = bf16_lo(w[i]) * r;
-        y[2 * i + 1] = bf16_hi(w[i]) * r;
-    }
-    if (__builtin_isinf(r)) {
-        // s * G underflowed: x * inf is +-inf (code 6) except 0 * inf, which
-        // is taken as a zero code with the sign of x.
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
-            y[2 * i] = a == 0.0f ? a : y[2 * i];
-            y[2 * i + 1] = b == 0.0f ? b : y[2 * i + 1];
-        }
-    }
-    uint32_t c = 0;
-    c = FP4_PACK2(c, y[0], y[1], 0);
-    c = FP4_PACK2(c, y[2], y[3], 1);
-    c = FP4_PACK2(c, y[4], y[5], 2);
-    c = FP4_PACK2(c, y[6], y[7], 3);
-    return c;
-}
-
 // ---- pass 2: block quantize ---------------------------------------------
 // Up to two independent tensors per launch (blockIdx.y), used by the KV
 // cache to write K and V together.  Rows of tensor j start at output row

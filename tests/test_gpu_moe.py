@@ -244,8 +244,15 @@ def test_moe_empty_and_deterministic():
     assert e.shape == (0, cfg.H)
 
 
-def test_static_globals_equal_dynamic():
-    cfg = synth.MoE(seed=34, E=4, k=2, H=256, I=128, T=33)
+@pytest.mark.parametrize("cfg", [synth.MoE(seed=34, E=4, k=2, H=256, I=128, T=33),
+                                 synth.MoE(seed=37, E=2, k=1, H=2048, I=512, T=12),
+                                 synth.MoE(seed=41, E=3, k=2, H=512, I=256, T=300, mx=True)],
+                         ids=["small", "gate-split", "tiles-mx"])
+def test_static_globals_equal_dynamic(cfg):
+    """Static globals equal to the dynamic ones give the same output; with a
+    static G_h the gate_up epilogue encodes h itself (tile, streaming and
+    K-split paths), so this also pins that encode to the quantize kernel."""
+    step(f"moe static globals E={cfg.E} H={cfg.H} I={cfg.I} T={cfg.T}")
     W = workloads.build_moe_weights(cfg, DEV)
     x = cfg.x(DEV)
     ids, w = workloads.routing(cfg, DEV)
@@ -253,3 +260,31 @@ def test_static_globals_equal_dynamic():
     sg = torch.stack([g["xq"].global_[0], g["hq"].global_[0]]).contiguous()
     out = nv.nvfp4_moe_grouped_gemm(x, ids, w, W.w13, W.w2, static_in_globals=sg)
     assert torch.equal(out, g["out"])
+
+
+@pytest.mark.parametrize("cfg,scale", [
+    (synth.MoE(seed=42, E=4, k=2, H=512, I=256, T=300), 1.0),     # 256/128-row tiles + streaming
+    (synth.MoE(seed=43, E=4, k=2, H=576, I=256, T=40), 1.0),      # K % 256 != 0: 32-row tiles
+    (synth.MoE(seed=44, E=8, k=2, H=1024, I=256, T=48, mx=True), 0.25),  # streaming, saturating G_h
+])
+def test_gate_up_q_equals_quantize_of_h(orc, cfg, scale):
+    """nvfp4_moe_gate_up_q (h encoded in the epilogue with a static G_h)
+    gives, byte for byte, nvfp4_quantize(h, static G_h) of the h that
+    nvfp4_moe_gate_up writes, and the oracle's quantization of that h."""
+    step(f"gate_up_q E={cfg.E} H={cfg.H} I={cfg.I} T={cfg.T} scale={scale}")
+    W = workloads.build_moe_weights(cfg, DEV)
+    x = cfg.x(DEV)
+    ids, _ = workloads.routing(cfg, DEV)
+    xq = nv.nvfp4_quantize(x)
+    perm, offsets, _ = nv.nvfp4_moe_route(ids, cfg.E)
+    h, hmax = nv.nvfp4_moe_gate_up(xq, perm, offsets, cfg.k, W.w13)
+    amax = float(np.uint32(hmax.item()).view(np.float32))
+    Gh = np.float32(orc.global_from_amax(amax) * scale)
+    g = torch.tensor([Gh], dtype=torch.float32, device=DEV)
+    hq = nv.nvfp4_moe_gate_up_q(xq, perm, offsets, cfg.k, W.w13, g)
+    ref = nv.nvfp4_quantize(h, static_global=g)
+    assert torch.equal(hq.packed, ref.packed)
+    assert torch.equal(hq.scales, ref.scales)
+    ho = orc.quantize(synth.bits(h.cpu()), static_G=Gh)
+    np.testing.assert_array_equal(u8(hq.packed)[0], ho.packed)
+    np.testing.assert_array_equal(u8(hq.scales)[0], ho.scales)
