@@ -276,6 +276,7 @@ def torch_index(a):
 
 def breakdown(args):
     """Other hot-path rows on their own configs (each timed with HIP events)."""
+    import ctypes
     import numpy as np
     import torch
     import precision_moe_gemm_amd as nv
@@ -386,6 +387,31 @@ def breakdown(args):
 
     # KV cache 262144 x 4 x 256
     c5 = synth.C5
+    log("breakdown: n-gram table gather-dequant")
+    # one of the 128 shards of a 20M-row x 2560 NVFP4 n-gram table; 16384 lookups
+    V, D, n = 20000000 // 128, 2560, 16384
+    tab = nv.NVFP4Tensor.empty(V, D, 1, dev)
+    for r0 in range(0, V, 16384):
+        r1 = min(V, r0 + 16384)
+        blk = synth.normal_bf16((r1 - r0, D), 0.05, (740, r0), dev)
+        nv.nvfp4_quantize(blk, static_global=torch.tensor([0.05 * 5 / 2688], device=dev),
+                          out=nv.NVFP4Tensor(tab.packed[:, r0:r1], tab.scales[:, r0:r1], tab.global_, r1 - r0, D, 1))
+    tab.global_.fill_(0.05 * 5 / 2688)
+    gids = torch.randint(0, V, (n,), dtype=torch.int32, device=dev, generator=torch.Generator(device=dev).manual_seed(741))
+    gout = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
+    lib = _lib.load()
+    tcs = tab.c()
+    f = lambda: lib.nvfp4_gather_dequantize(ctypes.byref(tcs), ctypes.c_void_p(gids.data_ptr()), n,
+                                            ctypes.c_void_p(gout.data_ptr()), _lib.BF16, ctypes.c_void_p(st.cuda_stream))
+    f()
+    ms = time_loop(f, it, st)
+    gb = n * D * (0.5625 + 2)
+    res["gather_dequant_ngram_shard_156250x2560_n16384"] = {
+        "ms": round(ms, 4), "GBps": gbs(gb, ms), "bytes_basis": "0.5625 B/elem read (codes + scales of the looked-up rows) + 2 B/elem bf16 written",
+        "frac_hbm": round(gbs(gb, ms) / PEAK_HBM_GBS, 4)}
+    del tab, gout, gids
+    torch.cuda.empty_cache()
+
     log("breakdown: KV cache")
     kk, vv = c5.k(dev), c5.v(dev)
     kc = nv.NVFP4Tensor.empty(c5.tokens * c5.heads, c5.dim, 1, dev)

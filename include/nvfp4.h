@@ -134,6 +134,19 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int6
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dtype, void* stream);
 
 /*
+ * Row gather-dequantize for NVFP4 embedding tables (page
+ * "Qwen3.8-Flash-Next-FP4-Local", section 2.1: the n-gram embedding table
+ * stored as NVFP4 with 16-element groups, rows of 2560 looked up per
+ * token): out[i] = dequantize(table row ids[i]) for i < n, out
+ * [n, cols] fp32 or bf16 with nvfp4_dequantize's value rule.  table: batch
+ * 1 (one shard, one global); ids: int32 [n] on the device.  An id outside
+ * [0, rows) gives a zero row and the sticky NVFP4_ERR_RANGE (the call itself
+ * returns OK).  n * cols / 8 must stay below 2^32 (else UNSUPPORTED).
+ */
+nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* ids, int64_t n,
+                                     void* out, nvfp4_dtype dtype, void* stream);
+
+/*
  * MXFP4 encode (OCP MX: blocks of 32 along the last dimension, UE8M0 scale
  * 2^(floor(log2 amax) - 2), E2M1 nearest-even codes saturating at 6; an
  * all-zero block stores scale byte 0) of a bf16 matrix [rows, cols].

@@ -202,6 +202,22 @@ def dequantize(t: NVFP4, want_bf16: bool = False):
     return (out, outb) if want_bf16 else out
 
 
+def gather_dequantize(t: NVFP4, ids, want_bf16: bool = False):
+    """Row gather of an NVFP4 embedding table, then dequantize (page
+    "Qwen3.8-Flash-Next-FP4-Local", section 2.1: rows of an NVFP4 n-gram
+    table looked up per token).  An id outside [0, rows) gives a zero row.
+    This is the definition written out: select the rows, dequantize them."""
+    ids = np.asarray(ids, dtype=np.int64)
+    R, K = t.shape
+    ok = (ids >= 0) & (ids < R)
+    src = np.where(ok, ids, 0)
+    sub = NVFP4(np.ascontiguousarray(t.packed[src]), np.ascontiguousarray(t.scales[src]), t.G)
+    res = dequantize(sub, want_bf16)
+    for a in (res if want_bf16 else (res,)):
+        a[~ok] = 0
+    return res
+
+
 def gemm_rows(A: NVFP4, W: NVFP4, a_rows=None, w_rows=None) -> np.ndarray:
     """Exact C = Ga*Gw*deq0(A[a_rows]) @ deq0(W[w_rows])^T as float64."""
     M, K = A.shape

@@ -22,6 +22,7 @@ __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
+    "nvfp4_gather_dequantize",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
     "nvfp4_recipe", "status_string",
 ]
@@ -129,6 +130,19 @@ def nvfp4_dequantize(t: NVFP4Tensor, dtype=torch.float32) -> torch.Tensor:
     tc = t.c()
     _check(_lib.load().nvfp4_dequantize(ctypes.byref(tc), _ptr(out), code, _stream(t.device)),
            "nvfp4_dequantize")
+    return out
+
+
+def nvfp4_gather_dequantize(table: NVFP4Tensor, ids: torch.Tensor, dtype=torch.bfloat16) -> torch.Tensor:
+    """Rows ids (int32 [n]) of an NVFP4 table, dequantized: [n, cols]."""
+    _need_cuda(ids)
+    assert ids.dtype == torch.int32 and ids.dim() == 1 and ids.is_contiguous()
+    n = ids.numel()
+    out = torch.empty((n, table.cols), dtype=dtype, device=table.device)
+    code = _lib.BF16 if dtype == torch.bfloat16 else _lib.F32
+    tc = table.c()
+    _check(_lib.load().nvfp4_gather_dequantize(ctypes.byref(tc), _ptr(ids), n, _ptr(out), code,
+                                               _stream(table.device)), "nvfp4_gather_dequantize")
     return out
 
 

@@ -46,6 +46,7 @@ SIGNATURES = {
     "nvfp4_workspace_size": (SZ, [ctypes.c_int, I64, I32, I32, I64, I64]),
     "nvfp4_quantize": (ST, [P, I64, I64, I64, P, TP, P, SZ, P]),
     "nvfp4_dequantize": (ST, [TP, P, ctypes.c_int, P]),
+    "nvfp4_gather_dequantize": (ST, [TP, P, I64, P, I32, P]),
     "mxfp4_quantize": (ST, [P, I64, I64, I64, P, P, P]),
     "mxfp4_to_nvfp4": (ST, [P, P, I64, I64, I64, TP, P, SZ, P]),
     "nvfp4_gemm": (ST, [TP, TP, P, ctypes.c_int, P, SZ, P]),

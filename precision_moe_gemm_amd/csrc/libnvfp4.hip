@@ -27,7 +27,7 @@ inline nvfp4_status launch_status()
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
+// number of 256-thread blocks for a grid-stride kernel that wants `work` threads (capped)
 // grid for a grid-stride streaming kernel over `work` items of 256 threads
 inline unsigned stream_grid(int64_t work, int64_t cap = 8192)
 {
@@ -528,6 +528,37 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dty
     else
         dequantize_kernel<false><<<grid, kQuantThreads, 0, S(stream)>>>(
             (const uint32_t*)in->packed, in->scales, in->global, nblk, in->rows * bpr, 0, out);
+    return launch_status();
+}
+
+nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* ids, int64_t n, void* out,
+                                     nvfp4_dtype dtype, void* stream)
+{
+    nvfp4_status s = check_tensor(table);
+    if (s != NVFP4_OK)
+        return s;
+    if (table->batch != 1)
+        return NVFP4_ERR_SHAPE;
+    if (n < 0)
+        return NVFP4_ERR_SHAPE;
+    if (n == 0 || table->cols == 0)
+        return NVFP4_OK;
+    if (!ids || !out || !aligned(out, 16) || !aligned(ids, 4))
+        return NVFP4_ERR_INVALID_ARG;
+    if (dtype != NVFP4_F32 && dtype != NVFP4_BF16)
+        return NVFP4_ERR_INVALID_ARG;
+    const int64_t hpr = table->cols / 8;
+    if (n * hpr >= ((int64_t)1 << 32) - 4 * kQuantThreads)
+        return NVFP4_ERR_UNSUPPORTED;
+    const unsigned grid = stream_grid(ceil_div(n * hpr, 4), 8192);  // 4 row slices of 8 per thread
+    if (dtype == NVFP4_BF16)
+        gather_dequant_kernel<true><<<grid, kQuantThreads, 0, S(stream)>>>(
+            (const uint32_t*)table->packed, table->scales, table->global, ids, (uint32_t)n, table->rows,
+            (uint32_t)hpr, out);
+    else
+        gather_dequant_kernel<false><<<grid, kQuantThreads, 0, S(stream)>>>(
+            (const uint32_t*)table->packed, table->scales, table->global, ids, (uint32_t)n, table->rows,
+            (uint32_t)hpr, out);
     return launch_status();
 }
 

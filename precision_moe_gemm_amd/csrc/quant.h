@@ -204,6 +204,64 @@ dequantize_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict
     }
 }
 
+// ---- row gather-dequantize (embedding tables) -------------------------------
+// out[i] = dequantize(table row ids[i]) for i < n, rows of `hpr` half-blocks
+// (cols / 8); the same value rule as dequantize_kernel.  An id outside
+// [0, rows) gives a zero output row and raises NVFP4_ERR_RANGE.  Work item
+// = one output half-block; four per thread per trip, loads first.
+template <bool kBf16>
+__global__ void __launch_bounds__(kQuantThreads)
+gather_dequant_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                      const float* __restrict__ global, const int32_t* __restrict__ ids, uint32_t n,
+                      int64_t rows, uint32_t hpr, void* __restrict__ out)
+{
+    constexpr int kU = 4;
+    const float G = *global;
+    const uint32_t nhalf = n * hpr;
+    const uint32_t chunk = kU * kQuantThreads;
+    for (uint32_t base = blockIdx.x * chunk; base < nhalf; base += gridDim.x * chunk) {
+        uint32_t c[kU], sb[kU];
+        bool ok[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const uint32_t hb = base + u * kQuantThreads + threadIdx.x;
+            const uint32_t i = (hb < nhalf ? hb : nhalf - 1) / hpr;
+            const uint32_t j = (hb < nhalf ? hb : nhalf - 1) - i * hpr;
+            const int32_t id = ids[i];
+            ok[u] = id >= 0 && id < rows;
+            const int64_t src = (int64_t)(ok[u] ? id : 0) * hpr + j;
+            c[u] = packed[src];
+            sb[u] = scales[src >> 1];
+            if (!ok[u] && hb < nhalf && j == 0)
+                raise_error(NVFP4_ERR_RANGE);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const uint32_t hb = base + u * kQuantThreads + threadIdx.x;
+            if (hb >= nhalf)
+                break;
+            const float sc = ok[u] ? e4m3_decode(sb[u]) : 0.0f;
+            const float2_t q[4] = {FP4_TO_F32X2(c[u], 0), FP4_TO_F32X2(c[u], 1), FP4_TO_F32X2(c[u], 2),
+                                   FP4_TO_F32X2(c[u], 3)};
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                v[2 * t] = ok[u] ? (q[t].x * sc) * G : 0.0f;
+                v[2 * t + 1] = ok[u] ? (q[t].y * sc) * G : 0.0f;
+            }
+            if (kBf16) {
+                __builtin_nontemporal_store((u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
+                                            (u32x4*)out + hb);
+            } else {
+                float4_t* o = (float4_t*)out + 2 * (int64_t)hb;
+                __builtin_nontemporal_store((float4_t){v[0], v[1], v[2], v[3]}, o);
+                __builtin_nontemporal_store((float4_t){v[4], v[5], v[6], v[7]}, o + 1);
+            }
+        }
+    }
+}
+
 // ---- scale audit: counts of {all, NaN pattern, zero/negative, 448} ---------
 __global__ void __launch_bounds__(kQuantThreads)
 audit_kernel(const uint8_t* __restrict__ scales, int64_t n, unsigned long long* __restrict__ counts)

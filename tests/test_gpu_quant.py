@@ -168,3 +168,34 @@ def test_host_errors():
     with pytest.raises(nv.NVFP4Error) as ei:
         nv.nvfp4_quantize(x, out=nv.NVFP4Tensor.empty(4, 16, 1, DEV))
     assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("R,D,n", [(1000, 2560, 700), (37, 64, 5), (513, 16, 1031)])
+def test_gather_dequantize_matches_oracle(orc, R, D, n):
+    """Row gather-dequantize of an NVFP4 embedding table (rows of 2560 as in
+    the n-gram table, plus small and ragged shapes): bit-exact against the
+    oracle for fp32 and bf16, repeated and unsorted ids."""
+    step(f"gather dequant R={R} D={D} n={n}")
+    xb = synth.bits(synth.normal_bf16((R, D), 0.05, (730, R, D)))
+    t = _gpu_q(xb)
+    ref = orc.quantize(xb)
+    ids = np.random.default_rng(R + n).integers(0, R, n).astype(np.int32)
+    gi = torch.from_numpy(ids).to(DEV)
+    f_ref, b_ref = orc.gather_dequantize(ref, ids, want_bf16=True)
+    f = nv.nvfp4_gather_dequantize(t, gi, torch.float32).cpu().numpy()
+    b = synth.bits(nv.nvfp4_gather_dequantize(t, gi, torch.bfloat16))
+    np.testing.assert_array_equal(f.view(np.uint32), f_ref.view(np.uint32))
+    np.testing.assert_array_equal(b, b_ref)
+
+
+def test_gather_dequantize_bad_ids_and_empty(orc):
+    xb = synth.bits(synth.normal_bf16((40, 128), 1.0, (731,)))
+    t = _gpu_q(xb)
+    ref = orc.quantize(xb)
+    ids = np.array([3, -1, 40, 39, 0, 1 << 30], np.int32)
+    nv.nvfp4_get_error()  # clear
+    f = nv.nvfp4_gather_dequantize(t, torch.from_numpy(ids).to(DEV), torch.float32).cpu().numpy()
+    assert nv.nvfp4_get_error() == 3  # NVFP4_ERR_RANGE
+    np.testing.assert_array_equal(f.view(np.uint32), orc.gather_dequantize(ref, ids).view(np.uint32))
+    e = nv.nvfp4_gather_dequantize(t, torch.zeros(0, dtype=torch.int32, device=DEV))
+    assert e.shape == (0, 128)

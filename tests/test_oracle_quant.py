@@ -249,3 +249,32 @@ def test_subnormal_scale_regime(orc):
     assert q.scales[0, 0] == 0x7E
     assert 0 < q.scales[0, 1] < 0x08  # subnormal E4M3
     assert q.scales[0, 3] == 0
+
+
+def test_gather_dequantize_selects_rows(orc):
+    """Gather-dequantize is the row selection of the dequantized table: ids
+    0..R-1 give the whole table, a repeated / shuffled list gives those rows
+    of it, and each element is e2m1 * e4m3 * G (brute force, exact for a
+    power-of-two G); ids outside [0, R) give zero rows."""
+    R, K = 37, 64
+    rng = np.random.default_rng(5)
+    packed = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 127, (R, K // 16), dtype=np.uint8)
+    t = orc.NVFP4(packed, scales, 0.25)
+    full = orc.dequantize(t)
+    assert np.array_equal(orc.gather_dequantize(t, np.arange(R)), full)
+    ids = np.array([5, 0, 36, 5, 17, 17, 2], np.int32)
+    g = orc.gather_dequantize(t, ids)
+    assert np.array_equal(g, full[ids])
+    mags = [float(m) for m in _e2m1_mags()]
+    e4 = [float(v) for v in _e4m3_table()]
+    for i, r in enumerate(ids):
+        for c in range(K):
+            nib = (packed[r, c // 2] >> (4 * (c & 1))) & 15
+            want = mags[nib & 7] * e4[scales[r, c // 16]] * 0.25 * (-1 if nib & 8 else 1)
+            assert g[i, c] == np.float32(want)
+    bad = orc.gather_dequantize(t, np.array([3, -1, R, 4], np.int32))
+    assert np.array_equal(bad[[0, 3]], full[[3, 4]]) and not bad[[1, 2]].any()
+    f, b = orc.gather_dequantize(t, ids, want_bf16=True)
+    assert np.array_equal(f, g)
+    assert np.array_equal(b, orc.dequantize(t, want_bf16=True)[1][ids])
