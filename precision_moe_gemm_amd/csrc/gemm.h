@@ -222,41 +222,47 @@ NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&ac
     const int rows_left = (int)(tc.row_end - wrow0);
     const int ld = (int)p.N;
     if (MODE == kModeGateUp && p.hq_global) {
-        // h straight to NVFP4 through LDS (free once the mainloop is done):
-        // the tile's bf16 h [BM, BN/2] goes to LDS, then each thread encodes
-        // whole 16-element blocks as the quantize kernel does
+        // h straight to NVFP4 through LDS (free once the mainloop is done),
+        // one wave row at a time: the waves of that row put their bf16 h
+        // [TM, BN/2] in LDS, then every thread encodes whole 16-element
+        // blocks as the quantize kernel does
         constexpr int HC = BN / 2;  // h columns of the tile
         uint16_t* hs = (uint16_t*)lds;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < FM; i++) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rr = wave_m * TM + i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
-#pragma unroll
-                for (int j = 0; j < FN / 2; j++) {
-                    const float gg = acc[i][j][r] * gscale;
-                    const float uu = acc[i][j + FN / 2][r] * gscale;
-                    hs[rr * HC + wave_n * (TN / 2) + j * 32 + ncol] = f32_to_bf16(silu_f(gg) * uu);
-                }
-            }
-        }
-        __syncthreads();
         const float Gh = *p.hq_global, six = 6.0f * Gh;
         const int64_t hcol0 = tc.nt * HC;
-        for (int b = threadIdx.x; b < WM * TM * (HC / 16); b += blockDim.x) {
-            const int row = b / (HC / 16), bc = b - row * (HC / 16);
-            const int64_t grow = tc.row_begin + row;
-            if (grow < tc.row_end) {
-                const u32x4 v0 = *(const u32x4*)(hs + row * HC + 16 * bc);
-                const u32x4 v1 = *(const u32x4*)(hs + row * HC + 16 * bc + 8);
-                const uint32_t a0 = absmax_bits8(v0), a1 = absmax_bits8(v1);
-                uint32_t sc;
-                const float rcp = block_scale(a0 > a1 ? a0 : a1, Gh, six, &sc);
-                const int64_t col = hcol0 + 16 * bc;
-                *(u32x2*)(p.hq_packed + grow * (p.N / 2) + col / 2) =
-                    (u32x2){encode_half(v0, rcp), encode_half(v1, rcp)};
-                p.hq_scales[grow * (p.N / 16) + col / 16] = (uint8_t)sc;
+#pragma unroll 1
+        for (int pm = 0; pm < WM; pm++) {
+            __syncthreads();
+            if (wave_m == pm) {
+#pragma unroll
+                for (int i = 0; i < FM; i++) {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int rr = i * 32 + (r & 3) + 8 * (r >> 2) + rsub;
+#pragma unroll
+                        for (int j = 0; j < FN / 2; j++) {
+                            const float gg = acc[i][j][r] * gscale;
+                            const float uu = acc[i][j + FN / 2][r] * gscale;
+                            hs[rr * HC + wave_n * (TN / 2) + j * 32 + ncol] = f32_to_bf16(silu_f(gg) * uu);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int b = threadIdx.x; b < TM * (HC / 16); b += blockDim.x) {
+                const int row = b / (HC / 16), bc = b - row * (HC / 16);
+                const int64_t grow = tc.row_begin + pm * TM + row;
+                if (grow < tc.row_end) {
+                    const u32x4 v0 = *(const u32x4*)(hs + row * HC + 16 * bc);
+                    const u32x4 v1 = *(const u32x4*)(hs + row * HC + 16 * bc + 8);
+                    const uint32_t a0 = absmax_bits8(v0), a1 = absmax_bits8(v1);
+                    uint32_t sc;
+                    const float rcp = block_scale(a0 > a1 ? a0 : a1, Gh, six, &sc);
+                    const int64_t col = hcol0 + 16 * bc;
+                    *(u32x2*)(p.hq_packed + grow * (p.N / 2) + col / 2) =
+                        (u32x2){encode_half(v0, rcp), encode_half(v1, rcp)};
+                    p.hq_scales[grow * (p.N / 16) + col / 16] = (uint8_t)sc;
+                }
             }
         }
     } else if (MODE == kModeGateUp) {
@@ -932,6 +938,337 @@ gemm_tile_kernel(GemmArgs p)
     if (s + 6 < nst)
         stage(s + 6, IntC<1>{});
     store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane, &lds_f[0][0]);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill mainloop with register decode (K a multiple of 256).
+//
+// Same tiles, waves and MFMA as gemm_tile_kernel, but no f16 tile in LDS:
+// every wave reads the packed codes of its own fragment rows from the LDS
+// staging and decodes them straight into MFMA operand registers.  Measured
+// on one wave per SIMD: a 16-byte LDS write stalls the issuing wave's MFMA
+// stream by about 35 cycles when VALU work is interleaved, while up to four
+// conversions per 32x32x16 MFMA issue in its shadow for free.  Decoding per
+// wave repeats each row's decode on the two waves that share it, which stays
+// within that budget, and removes the f16 writes, the f16 fragment reads and
+// three of every four barriers.
+//
+// K is walked in groups of 128 elements.  Inside a group the K order of the
+// MFMA is permuted identically for A and W: lane half g (lane / 32) of
+// k-step j (0..7) takes the 8 elements of dword j % 4 of 16-byte chunk
+// g + 2 (j / 4) of the row's 64 code bytes, so each lane reads one chunk per
+// row per four k-steps, and those 32 elements share two scale bytes.  Codes
+// are copied by the LDS DMA path into four group buffers (layout tpos), two
+// groups ahead; the scale bytes of a pair of groups (16 per row) go to two
+// pair buffers.  One barrier per group, after its fourth k-step, publishes
+// the next group's staging (each wave first waits for its own copies) and
+// frees the buffer that the group after next is copied into.  Every buffer
+// is its own LDS array so that reads from one never wait for copies into
+// another.
+// ---------------------------------------------------------------------------
+constexpr int kRGrpK = 128;  // K elements per group
+
+template <int BM, int BN, int MODE, bool P2>
+__global__ void __launch_bounds__(256)
+gemm_rtile_kernel(GemmArgs p)
+{
+    constexpr int WM = 2, WN = 2, NW = 4;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ROWS = BM + BN;
+    constexpr int NJ = (ROWS + 16 * NW - 1) / (16 * NW);  // code copies per wave per group
+    constexpr int SROWS = NJ * NW * 16;                    // staged code rows (>= ROWS)
+    constexpr int NS = (ROWS + 64 * NW - 1) / (64 * NW);   // scale copies per wave per group pair
+    constexpr int SSROWS = NS * NW * 64;                   // staged scale rows (>= ROWS)
+    constexpr int CB = SROWS * kTGRow;                     // bytes per code buffer
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && NJ % 2 == 0, "tile shape");
+    static_assert(MODE != kModeGateUp || FN % 2 == 0, "gate_up pairs gate and up fragments");
+    static_assert(TM * (BN / 2) * 2 <= CB, "an h pass of the epilogue fits one code buffer");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds_c0[CB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_c1[CB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_c2[CB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_c3[CB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_s0[SSROWS * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_s1[SSROWS * 16];
+    auto cbuf = [&](auto b_tag) -> uint8_t* {
+        constexpr int B = decltype(b_tag)::value & 3;
+        return B == 0 ? lds_c0 : B == 1 ? lds_c1 : B == 2 ? lds_c2 : lds_c3;
+    };
+    auto sbuf = [&](auto b_tag) -> uint8_t* { return (decltype(b_tag)::value & 1) ? lds_s1 : lds_s0; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave / WN, wave_n = wave % WN;
+
+    TileCoord tc;
+    if (!tile_coord<BM, MODE>(p, tc))
+        return;
+    const int e = tc.e;
+    const int64_t K = p.K;
+    const int64_t kpb = K / 2, kpsb = K / 16;  // packed / scale bytes per row
+    const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
+    const uint8_t* wp = p.w_packed + (int64_t)e * w_rows * kpb;
+    const uint8_t* wsc = p.w_scales + (int64_t)e * w_rows * kpsb;
+    auto matrix_row = [&](int r) -> int64_t {
+        return r < BM ? tile_a_row<MODE>(p, tc, r) : tile_w_row<BN, TN, MODE>(p, tc, r - BM);
+    };
+    const int64_t ngr = K / kRGrpK;  // even
+    const int64_t npr = ngr / 2;
+
+    // ---- code copies: copy j of this wave fills bytes [1024 (NJ wave + j),
+    // +1024) of a group buffer, lane l the 16 bytes at 16 l: line
+    // q = 8 (NJ wave + j) + l / 8, slot l % 8, i.e. the (row, chunk) that tpos
+    // places there
+    int32_t srow[NJ];
+    int scq[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        const int q = 8 * (NJ * wave + j) + (lane >> 3);
+        const int hc = (lane & 7) ^ ((q ^ (q >> 1)) & 7);  // 4 (r % 2) + c
+        int r = 2 * q + (hc >> 2);
+        if (r >= ROWS)
+            r = ROWS - 1;
+        srow[j] = (int32_t)matrix_row(r);
+        scq[j] = hc & 3;
+    }
+    // ---- scale copies: copy j of this wave fills 16-byte row slots
+    // [64 (NS wave + j), +64) of a pair buffer with the 16 scale bytes of a
+    // pair of groups (slots past the last row repeat it)
+    const uint8_t* ssrc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        int r = 64 * (NS * wave + j) + lane;
+        if (r >= ROWS)
+            r = ROWS - 1;
+        ssrc[j] = (r < BM ? p.a_scales : wsc) + matrix_row(r) * kpsb;
+    }
+    // copies [J0, J1) of the codes of group G (clamped to the last) into buffer B
+    auto issue_codes = [&](int64_t G, auto b_tag, auto j0_tag, auto j1_tag) {
+        constexpr int J0 = decltype(j0_tag)::value, J1 = decltype(j1_tag)::value;
+        const int64_t cb = (G < ngr ? G : ngr - 1) * kTGRow;
+        uint8_t* dst = cbuf(b_tag);
+#pragma unroll
+        for (int j = J0; j < J1; j++) {
+            const bool is_a = 16 * (NJ * wave + j) < BM;  // uniform per copy
+            const uint8_t* src = (is_a ? p.a_packed : wp) + (int64_t)srow[j] * kpb + cb + 16 * scq[j];
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + (NJ * wave + j) * 1024), 16,
+                                             0, 0);
+        }
+    };
+    // the scale copies of group pair Q (clamped to the last) into pair buffer B
+    auto issue_scales = [&](int64_t Q, auto b_tag) {
+        const int64_t sb = (Q < npr ? Q : npr - 1) * 16;
+        uint8_t* dst = sbuf(b_tag);
+#pragma unroll
+        for (int j = 0; j < NS; j++)
+            __builtin_amdgcn_global_load_lds((const void*)(ssrc[j] + sb), (lds_ptr_t)(dst + (NS * wave + j) * 1024),
+                                             16, 0, 0);
+    };
+
+    // ---- this lane's fragment rows: A rows ra + 32 i, W rows rw + 32 j.
+    // They differ by multiples of 32, which keeps the line swizzle and the
+    // row parity, so one chunk offset per half serves all of them.
+    const int frow = lane & 31;
+    const int g = lane >> 5;
+    const int ra = wave_m * TM + frow, rw = BM + wave_n * TN + frow;
+    const int lsw = tline_sw(frow), par = frow & 1;
+    const int aoff0 = 64 * (ra & ~1) + 16 * ((4 * par + g) ^ lsw);
+    const int aoff1 = 64 * (ra & ~1) + 16 * ((4 * par + g + 2) ^ lsw);
+    const int woff0 = 64 * (rw & ~1) + 16 * ((4 * par + g) ^ lsw);
+    const int woff1 = 64 * (rw & ~1) + 16 * ((4 * par + g + 2) ^ lsw);
+    const uint32_t sshift = 16 * g;  // this lane's two scale bytes of a chunk
+
+    u32x4 cA[FM], cW[FN];  // codes, chunk g of the group (k-steps 0-3)
+    u32x4 hA[FM], hW[FN];  // codes, chunk g + 2 (k-steps 4-7)
+    u32x2 sA[FM], sW[FN];  // scale bytes of the group (8 per row)
+    u32x2 nA[FM], nW[FN];  // ... of the next group
+    half2_t vA[FM];        // f16 scales of the two blocks of the current chunk
+    half2_t vWh[FN];       // (W, general scales)
+    float vW0[FN], vW1[FN];  // (W, power-of-two scales: the conversion's operand)
+    half8_t fa[2][FM], fw[2][FN];
+
+    auto read_half = [&](const uint8_t* buf, int ao, int wo, u32x4 (&da)[FM], u32x4 (&dw)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            da[i] = *(const u32x4*)(buf + ao + 2048 * i);
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            dw[j] = *(const u32x4*)(buf + wo + 2048 * j);
+    };
+    auto read_scales = [&](const uint8_t* buf, u32x2 (&da)[FM], u32x2 (&dw)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            da[i] = *(const u32x2*)(buf + 16 * (ra + 32 * i));
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            dw[j] = *(const u32x2*)(buf + 16 * (rw + 32 * j));
+    };
+    // scale values of chunk half H of a group from its 8 scale bytes per row
+    auto prep_scales = [&](auto h_tag, const u32x2 (&ba)[FM], const u32x2 (&bw)[FN]) {
+        constexpr int H = decltype(h_tag)::value;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            vA[i] = scales2<0>((H ? ba[i].y : ba[i].x) >> sshift);
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const uint32_t w = (H ? bw[j].y : bw[j].x) >> sshift;
+            if (P2) {
+                vW0[j] = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+                vW1[j] = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+            } else {
+                vWh[j] = scales2<0>(w);
+            }
+        }
+    };
+    // operands of k-step KS (of 8) into operand set S
+    auto decode_ks = [&](auto ks_tag, auto s_tag) {
+        constexpr int KS = decltype(ks_tag)::value & 7, S = decltype(s_tag)::value, D = KS & 3;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const u32x4 c = KS < 4 ? cA[i] : hA[i];
+            const uint32_t cw = D == 0 ? c.x : D == 1 ? c.y : D == 2 ? c.z : c.w;
+            fa[S][i] = __builtin_bit_cast(half8_t, decode_chunk(cw, (D >> 1) ? vA[i].y : vA[i].x));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const u32x4 c = KS < 4 ? cW[j] : hW[j];
+            const uint32_t cw = D == 0 ? c.x : D == 1 ? c.y : D == 2 ? c.z : c.w;
+            if (P2)
+                fw[S][j] = __builtin_bit_cast(half8_t, decode_chunk_p2(cw, (D >> 1) ? vW1[j] : vW0[j]));
+            else
+                fw[S][j] = __builtin_bit_cast(half8_t, decode_chunk(cw, (D >> 1) ? vWh[j].y : vWh[j].x));
+        }
+    };
+
+    float16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            acc[i][j] = (float16_t){};
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[slot][i], fw[slot][j], acc[i][j], 0, 0, 0);
+    };
+    // interleave: after each MFMA up to V VALU and, at chosen slots, one
+    // LDS read or one copy
+    auto interleave = [&](auto v_tag, auto nds_tag, auto ncp_tag) {
+        constexpr int V = decltype(v_tag)::value, NDS = decltype(nds_tag)::value, NCP = decltype(ncp_tag)::value;
+#pragma unroll
+        for (int m = 0; m < FM * FN; m++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (m < NDS)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, V, 0);      // VALU
+            if (NCP > 0 && m % (FM * FN / (NCP > 0 ? NCP : 1)) == FM * FN / (NCP > 0 ? NCP : 1) / 2)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (copy)
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: groups 0 and 1 and scale pair 0 staged, group 0 read,
+    // the first half of the copies of group 2 and scale pair 1 issued, the
+    // operands of k-step 0 decoded
+    issue_codes(0, IntC<0>{}, IntC<0>{}, IntC<NJ>{});
+    issue_codes(1, IntC<1>{}, IntC<0>{}, IntC<NJ>{});
+    issue_scales(0, IntC<0>{});
+    wait_vm<0>();
+    __syncthreads();
+    read_half(lds_c0, aoff0, woff0, cA, cW);
+    read_scales(lds_s0, sA, sW);
+    issue_codes(2, IntC<2>{}, IntC<0>{}, IntC<NJ / 2>{});
+    issue_scales(1, IntC<1>{});
+    prep_scales(IntC<0>{}, sA, sW);
+    decode_ks(IntC<0>{}, IntC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- group G with T = G mod 4 (compile time): buffers, copy targets and
+    // wait counts follow from T
+    constexpr int NH = NJ / 2;
+    auto group = [&](int64_t G, auto t_tag) {
+        constexpr int T = decltype(t_tag)::value;
+        constexpr int T1 = (T + 1) & 3;
+        // copies [CK(j), CK(j+1)) of a half window go with k-step j of 4
+#define RT_CK(j) (((j) * NH) / 4)
+        // k-step 0: the chunk g + 2 reads of this group first
+        read_half(cbuf(IntC<T>{}), aoff1, woff1, hA, hW);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        decode_ks(IntC<1>{}, IntC<1>{});
+        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(0)>{}, IntC<NH + RT_CK(1)>{});
+        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(1) - RT_CK(0)>{});
+        // k-steps 1, 2
+        mfmas(1);
+        decode_ks(IntC<2>{}, IntC<0>{});
+        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(1)>{}, IntC<NH + RT_CK(2)>{});
+        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(2) - RT_CK(1)>{});
+        mfmas(0);
+        decode_ks(IntC<3>{}, IntC<1>{});
+        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(2)>{}, IntC<NH + RT_CK(3)>{});
+        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(3) - RT_CK(2)>{});
+        // k-step 3, then the barrier that publishes group G + 1
+        mfmas(1);
+        prep_scales(IntC<1>{}, sA, sW);
+        decode_ks(IntC<4>{}, IntC<0>{});
+        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(3)>{}, IntC<NJ>{});
+        interleave(IntC<5>{}, IntC<0>{}, IntC<NJ - NH - RT_CK(3)>{});
+        // group G + 1 was copied two half windows ago; the copies of group
+        // G + 2 (and, for even G, of scale pair G / 2 + 1) may stay in flight
+        wait_vm<NJ + ((T & 1) == 0 ? NS : 0)>();
+        wait_lgkm0();
+        lds_barrier();
+        read_half(cbuf(IntC<T1>{}), aoff0, woff0, cA, cW);
+        read_scales(sbuf(IntC<(T1 >> 1)>{}) + 8 * (T1 & 1), nA, nW);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-steps 4-7 with the first half of the copies of group G + 3 (and,
+        // for odd G, scale pair (G + 3) / 2)
+        mfmas(0);
+        decode_ks(IntC<5>{}, IntC<1>{});
+        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(0)>{}, IntC<RT_CK(1)>{});
+        if (T & 1)
+            issue_scales((G + 3) >> 1, IntC<(((T + 3) >> 1) & 1)>{});
+        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(1) - RT_CK(0) + ((T & 1) ? NS : 0)>{});
+        mfmas(1);
+        decode_ks(IntC<6>{}, IntC<0>{});
+        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(1)>{}, IntC<RT_CK(2)>{});
+        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(2) - RT_CK(1)>{});
+        mfmas(0);
+        decode_ks(IntC<7>{}, IntC<1>{});
+        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(2)>{}, IntC<RT_CK(3)>{});
+        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(3) - RT_CK(2)>{});
+        mfmas(1);
+        prep_scales(IntC<0>{}, nA, nW);
+        decode_ks(IntC<0>{}, IntC<0>{});  // k-step 0 of group G + 1 (past the end: unused)
+        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(3)>{}, IntC<NH>{});
+        interleave(IntC<5>{}, IntC<0>{}, IntC<NH - RT_CK(3)>{});
+#undef RT_CK
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            sA[i] = nA[i];
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            sW[j] = nW[j];
+    };
+    int64_t G = 0;
+    for (; G + 4 <= ngr; G += 4) {
+        group(G, IntC<0>{});
+        group(G + 1, IntC<1>{});
+        group(G + 2, IntC<2>{});
+        group(G + 3, IntC<3>{});
+    }
+    if (G < ngr) {
+        group(G, IntC<0>{});
+        group(G + 1, IntC<1>{});
+    }
+    // copies past the end are still in flight into the buffers
+    wait_vm<0>();
+    __syncthreads();
+    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane, lds_c0);
 }
 
 }  // namespace nvfp4

@@ -126,10 +126,16 @@ nvfp4_status launch_tile(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     blocks = ceil_div(blocks, 8) * 8;
     if (blocks > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    if (p.w_pow2)
+    if (p.K >= 256 && p.K % 256 == 0) {
+        if (p.w_pow2)
+            gemm_rtile_kernel<BM, BN, MODE, true><<<(unsigned)blocks, 256, 0, st>>>(p);
+        else
+            gemm_rtile_kernel<BM, BN, MODE, false><<<(unsigned)blocks, 256, 0, st>>>(p);
+    } else if (p.w_pow2) {
         gemm_tile_kernel<BM, BN, MODE, true><<<(unsigned)blocks, 256, 0, st>>>(p);
-    else
+    } else {
         gemm_tile_kernel<BM, BN, MODE, false><<<(unsigned)blocks, 256, 0, st>>>(p);
+    }
     return launch_status();
 }
 
