@@ -24,6 +24,8 @@
 // conflicts).  Waves read MFMA fragments (8 f16 per lane) from the current
 // tile and issue v_mfma_f32_32x32x16_f16 while decoding the next stage.
 #pragma once
+#include <utility>
+
 #include "common.h"
 
 namespace nvfp4 {
@@ -132,6 +134,18 @@ template <int V>
 struct IntC {
     static constexpr int value = V;
 };
+
+// f(IntC<0>{}), ..., f(IntC<N-1>{}) in order
+template <class F, int... I>
+NVFP4_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(IntC<I>{}), ...);
+}
+template <int N, class F>
+NVFP4_DEV void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 NVFP4_DEV float silu_f(float g)
 {
@@ -968,6 +982,20 @@ gemm_tile_kernel(GemmArgs p)
 // ---------------------------------------------------------------------------
 constexpr int kRGrpK = 128;  // K elements per group
 
+// true when f maps 0..n-1 onto 0..n-1 one to one
+template <class F>
+constexpr bool rt_is_perm(F f, int n)
+{
+    for (int v = 0; v < n; v++) {
+        int hits = 0;
+        for (int x = 0; x < n; x++)
+            hits += f(x) == v;
+        if (hits != 1)
+            return false;
+    }
+    return true;
+}
+
 template <int BM, int BN, int MODE, bool P2>
 __global__ void __launch_bounds__(256)
 gemm_rtile_kernel(GemmArgs p)
@@ -1087,60 +1115,64 @@ gemm_rtile_kernel(GemmArgs p)
     half2_t vA[FM];        // f16 scales of the two blocks of the current chunk
     half2_t vWh[FN];       // (W, general scales)
     float vW0[FN], vW1[FN];  // (W, power-of-two scales: the conversion's operand)
-    half8_t fa[2][FM], fw[2][FN];
+    uint32_t oa[2][FM][4], ow[2][FN][4];  // MFMA operands (8 f16 each), two sets
 
-    auto read_half = [&](const uint8_t* buf, int ao, int wo, u32x4 (&da)[FM], u32x4 (&dw)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            da[i] = *(const u32x4*)(buf + ao + 2048 * i);
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-            dw[j] = *(const u32x4*)(buf + wo + 2048 * j);
-    };
-    auto read_scales = [&](const uint8_t* buf, u32x2 (&da)[FM], u32x2 (&dw)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            da[i] = *(const u32x2*)(buf + 16 * (ra + 32 * i));
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-            dw[j] = *(const u32x2*)(buf + 16 * (rw + 32 * j));
-    };
-    // scale values of chunk half H of a group from its 8 scale bytes per row
-    auto prep_scales = [&](auto h_tag, const u32x2 (&ba)[FM], const u32x2 (&bw)[FN]) {
-        constexpr int H = decltype(h_tag)::value;
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            vA[i] = scales2<0>((H ? ba[i].y : ba[i].x) >> sshift);
-#pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const uint32_t w = (H ? bw[j].y : bw[j].x) >> sshift;
+    // MFMA slot m of a k-step is followed by decode units [U0(m), U0(m+1)):
+    // unit u decodes half u % 2 (4 of the 8 f16) of operand row u / 2, rows
+    // taken A, W, A, W, ... then the remaining W rows
+    constexpr int NM = FM * FN, NU = 2 * (FM + FN);
+    constexpr auto unit_row = [](int rho) { return rho < 2 * FM ? ((rho & 1) ? FM + (rho >> 1) : (rho >> 1)) : rho; };
+    static_assert(rt_is_perm(unit_row, FM + FN), "decode units cover every operand row once");
+
+    // scale values of half H of a group for row R (A rows 0..FM-1, then W)
+    auto prep_row = [&](auto h_tag, auto r_tag, const u32x2 (&ba)[FM], const u32x2 (&bw)[FN]) {
+        constexpr int H = decltype(h_tag)::value, R = decltype(r_tag)::value;
+        if constexpr (R < FM) {
+            vA[R] = scales2<0>((H ? ba[R].y : ba[R].x) >> sshift);
+        } else {
+            constexpr int J = R - FM;
+            const uint32_t w = (H ? bw[J].y : bw[J].x) >> sshift;
             if (P2) {
-                vW0[j] = __builtin_amdgcn_cvt_f32_fp8(w, 0);
-                vW1[j] = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+                vW0[J] = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+                vW1[J] = __builtin_amdgcn_cvt_f32_fp8(w, 1);
             } else {
-                vWh[j] = scales2<0>(w);
+                vWh[J] = scales2<0>(w);
             }
         }
     };
-    // operands of k-step KS (of 8) into operand set S
-    auto decode_ks = [&](auto ks_tag, auto s_tag) {
-        constexpr int KS = decltype(ks_tag)::value & 7, S = decltype(s_tag)::value, D = KS & 3;
-#pragma unroll
-        for (int i = 0; i < FM; i++) {
-            const u32x4 c = KS < 4 ? cA[i] : hA[i];
+    // decode unit U of k-step KS into operand set S
+    auto decode_unit = [&](auto ks_tag, auto s_tag, auto u_tag) {
+        constexpr int KS = decltype(ks_tag)::value & 7, S = decltype(s_tag)::value, U = decltype(u_tag)::value;
+        constexpr int R = unit_row(U >> 1), HF = U & 1, D = KS & 3;
+        if constexpr (R < FM) {
+            const u32x4 c = KS < 4 ? cA[R] : hA[R];
             const uint32_t cw = D == 0 ? c.x : D == 1 ? c.y : D == 2 ? c.z : c.w;
-            fa[S][i] = __builtin_bit_cast(half8_t, decode_chunk(cw, (D >> 1) ? vA[i].y : vA[i].x));
-        }
-#pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const u32x4 c = KS < 4 ? cW[j] : hW[j];
+            const _Float16 sc = (D >> 1) ? vA[R].y : vA[R].x;
+            const half2_t ss = {sc, sc};
+            oa[S][R][2 * HF] =
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2 * HF) * ss);
+            oa[S][R][2 * HF + 1] =
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2 * HF + 1) * ss);
+        } else {
+            constexpr int J = R - FM;
+            const u32x4 c = KS < 4 ? cW[J] : hW[J];
             const uint32_t cw = D == 0 ? c.x : D == 1 ? c.y : D == 2 ? c.z : c.w;
-            if (P2)
-                fw[S][j] = __builtin_bit_cast(half8_t, decode_chunk_p2(cw, (D >> 1) ? vW1[j] : vW0[j]));
-            else
-                fw[S][j] = __builtin_bit_cast(half8_t, decode_chunk(cw, (D >> 1) ? vWh[j].y : vWh[j].x));
+            if (P2) {
+                const float sc = (D >> 1) ? vW1[J] : vW0[J];
+                ow[S][J][2 * HF] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 2 * HF));
+                ow[S][J][2 * HF + 1] =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 2 * HF + 1));
+            } else {
+                const _Float16 sc = (D >> 1) ? vWh[J].y : vWh[J].x;
+                const half2_t ss = {sc, sc};
+                ow[S][J][2 * HF] =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2 * HF) * ss);
+                ow[S][J][2 * HF + 1] =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2 * HF + 1) * ss);
+            }
         }
     };
+    auto operand = [](const uint32_t (&o)[4]) { return __builtin_bit_cast(half8_t, (u32x4){o[0], o[1], o[2], o[3]}); };
 
     float16_t acc[FM][FN];
 #pragma unroll
@@ -1148,28 +1180,33 @@ gemm_rtile_kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < FN; j++)
             acc[i][j] = (float16_t){};
-    auto mfmas = [&](int slot) {
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-#pragma unroll
-            for (int j = 0; j < FN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[slot][i], fw[slot][j], acc[i][j], 0, 0, 0);
+
+    // One k-step: MFMA slot m of operand set S, then the decode units of
+    // slot m for k-step KN into set S ^ 1 (preceded, at a row's first unit,
+    // by that row's scale values of half PH when PH >= 0: half 1 from this
+    // group's bytes, half 0 from the next group's), then extra(m) (LDS reads
+    // or copies placed at that slot).  The fences keep this order.
+    auto kstep = [&](auto s_tag, auto kn_tag, auto ph_tag, auto&& extra) {
+        constexpr int S = decltype(s_tag)::value, PH = decltype(ph_tag)::value;
+        static_for<NM>([&](auto m_tag) {
+            constexpr int m = decltype(m_tag)::value;
+            constexpr int i = m / FN, j = m % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(operand(oa[S][i]), operand(ow[S][j]), acc[i][j], 0, 0, 0);
+            static_for<(m + 1) * NU / NM - m * NU / NM>([&](auto k_tag) {
+                constexpr int U = m * NU / NM + decltype(k_tag)::value;
+                if constexpr (PH >= 0 && (U & 1) == 0) {
+                    if constexpr (PH == 1)
+                        prep_row(IntC<1>{}, IntC<unit_row(U >> 1)>{}, sA, sW);
+                    else
+                        prep_row(IntC<0>{}, IntC<unit_row(U >> 1)>{}, nA, nW);
+                }
+                decode_unit(kn_tag, IntC<S ^ 1>{}, IntC<U>{});
+            });
+            extra(m_tag);
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
-    // interleave: after each MFMA up to V VALU and, at chosen slots, one
-    // LDS read or one copy
-    auto interleave = [&](auto v_tag, auto nds_tag, auto ncp_tag) {
-        constexpr int V = decltype(v_tag)::value, NDS = decltype(nds_tag)::value, NCP = decltype(ncp_tag)::value;
-#pragma unroll
-        for (int m = 0; m < FM * FN; m++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            if (m < NDS)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, V, 0);      // VALU
-            if (NCP > 0 && m % (FM * FN / (NCP > 0 ? NCP : 1)) == FM * FN / (NCP > 0 ? NCP : 1) / 2)
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (copy)
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
+    auto none = [](auto) {};
 
     // ---- prologue: groups 0 and 1 and scale pair 0 staged, group 0 read,
     // the first half of the copies of group 2 and scale pair 1 issued, the
@@ -1179,73 +1216,118 @@ gemm_rtile_kernel(GemmArgs p)
     issue_scales(0, IntC<0>{});
     wait_vm<0>();
     __syncthreads();
-    read_half(lds_c0, aoff0, woff0, cA, cW);
-    read_scales(lds_s0, sA, sW);
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+        cA[i] = *(const u32x4*)(lds_c0 + aoff0 + 2048 * i);
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+        cW[j] = *(const u32x4*)(lds_c0 + woff0 + 2048 * j);
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+        nA[i] = *(const u32x2*)(lds_s0 + 16 * (ra + 32 * i));
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+        nW[j] = *(const u32x2*)(lds_s0 + 16 * (rw + 32 * j));
     issue_codes(2, IntC<2>{}, IntC<0>{}, IntC<NJ / 2>{});
     issue_scales(1, IntC<1>{});
-    prep_scales(IntC<0>{}, sA, sW);
-    decode_ks(IntC<0>{}, IntC<0>{});
+    static_for<NU>([&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;
+        if constexpr ((U & 1) == 0)
+            prep_row(IntC<0>{}, IntC<unit_row(U >> 1)>{}, nA, nW);
+        decode_unit(IntC<0>{}, IntC<0>{}, u_tag);
+    });
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+        sA[i] = nA[i];
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+        sW[j] = nW[j];
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- group G with T = G mod 4 (compile time): buffers, copy targets and
     // wait counts follow from T
     constexpr int NH = NJ / 2;
+    constexpr int CPS = NM / 2;  // the slot that carries a k-step's copies
     auto group = [&](int64_t G, auto t_tag) {
         constexpr int T = decltype(t_tag)::value;
         constexpr int T1 = (T + 1) & 3;
-        // copies [CK(j), CK(j+1)) of a half window go with k-step j of 4
-#define RT_CK(j) (((j) * NH) / 4)
-        // k-step 0: the chunk g + 2 reads of this group first
-        read_half(cbuf(IntC<T>{}), aoff1, woff1, hA, hW);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        decode_ks(IntC<1>{}, IntC<1>{});
-        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(0)>{}, IntC<NH + RT_CK(1)>{});
-        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(1) - RT_CK(0)>{});
-        // k-steps 1, 2
-        mfmas(1);
-        decode_ks(IntC<2>{}, IntC<0>{});
-        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(1)>{}, IntC<NH + RT_CK(2)>{});
-        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(2) - RT_CK(1)>{});
-        mfmas(0);
-        decode_ks(IntC<3>{}, IntC<1>{});
-        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(2)>{}, IntC<NH + RT_CK(3)>{});
-        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(3) - RT_CK(2)>{});
-        // k-step 3, then the barrier that publishes group G + 1
-        mfmas(1);
-        prep_scales(IntC<1>{}, sA, sW);
-        decode_ks(IntC<4>{}, IntC<0>{});
-        issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(3)>{}, IntC<NJ>{});
-        interleave(IntC<5>{}, IntC<0>{}, IntC<NJ - NH - RT_CK(3)>{});
-        // group G + 1 was copied two half windows ago; the copies of group
-        // G + 2 (and, for even G, of scale pair G / 2 + 1) may stay in flight
+        const uint8_t* cb = cbuf(IntC<T>{});
+        const uint8_t* cb1 = cbuf(IntC<T1>{});
+        const uint8_t* sb1 = sbuf(IntC<(T1 >> 1)>{}) + 8 * (T1 & 1);
+        // copies [CK(q), CK(q+1)) of a half window go with its k-step q of 4
+#define RT_CK(q) (((q) * NH) / 4)
+        // k-step 0, with the reads of the chunk g + 2 codes of this group
+        kstep(IntC<0>{}, IntC<1>{}, IntC<-1>{}, [&](auto m_tag) {
+            constexpr int m = decltype(m_tag)::value;
+            if constexpr (m < FM)
+                hA[m] = *(const u32x4*)(cb + aoff1 + 2048 * m);
+            else if constexpr (m < FM + FN)
+                hW[m - FM] = *(const u32x4*)(cb + woff1 + 2048 * (m - FM));
+            if constexpr (m == CPS)
+                issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(0)>{}, IntC<NH + RT_CK(1)>{});
+        });
+        kstep(IntC<1>{}, IntC<2>{}, IntC<-1>{}, [&](auto m_tag) {
+            if constexpr (decltype(m_tag)::value == CPS)
+                issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(1)>{}, IntC<NH + RT_CK(2)>{});
+        });
+        kstep(IntC<0>{}, IntC<3>{}, IntC<-1>{}, [&](auto m_tag) {
+            if constexpr (decltype(m_tag)::value == CPS)
+                issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(2)>{}, IntC<NH + RT_CK(3)>{});
+        });
+        kstep(IntC<1>{}, IntC<4>{}, IntC<1>{}, [&](auto m_tag) {
+            if constexpr (decltype(m_tag)::value == CPS)
+                issue_codes(G + 2, IntC<(T + 2) & 3>{}, IntC<NH + RT_CK(3)>{}, IntC<NJ>{});
+        });
+        // group G + 1 was copied a whole window ago; the copies of group G + 2
+        // (and, for even G, of scale pair G / 2 + 1) may stay in flight
         wait_vm<NJ + ((T & 1) == 0 ? NS : 0)>();
         wait_lgkm0();
         lds_barrier();
-        read_half(cbuf(IntC<T1>{}), aoff0, woff0, cA, cW);
-        read_scales(sbuf(IntC<(T1 >> 1)>{}) + 8 * (T1 & 1), nA, nW);
         __builtin_amdgcn_sched_barrier(0);
-        // k-steps 4-7 with the first half of the copies of group G + 3 (and,
-        // for odd G, scale pair (G + 3) / 2)
-        mfmas(0);
-        decode_ks(IntC<5>{}, IntC<1>{});
-        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(0)>{}, IntC<RT_CK(1)>{});
-        if (T & 1)
-            issue_scales((G + 3) >> 1, IntC<(((T + 3) >> 1) & 1)>{});
-        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(1) - RT_CK(0) + ((T & 1) ? NS : 0)>{});
-        mfmas(1);
-        decode_ks(IntC<6>{}, IntC<0>{});
-        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(1)>{}, IntC<RT_CK(2)>{});
-        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(2) - RT_CK(1)>{});
-        mfmas(0);
-        decode_ks(IntC<7>{}, IntC<1>{});
-        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(2)>{}, IntC<RT_CK(3)>{});
-        interleave(IntC<4>{}, IntC<0>{}, IntC<RT_CK(3) - RT_CK(2)>{});
-        mfmas(1);
-        prep_scales(IntC<0>{}, nA, nW);
-        decode_ks(IntC<0>{}, IntC<0>{});  // k-step 0 of group G + 1 (past the end: unused)
-        issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(3)>{}, IntC<NH>{});
-        interleave(IntC<5>{}, IntC<0>{}, IntC<NH - RT_CK(3)>{});
+        // k-step 4, with the reads of group G + 1 (chunk g, scales) and the
+        // first copies of group G + 3 (and, for odd G, scale pair (G + 3) / 2)
+        kstep(IntC<0>{}, IntC<5>{}, IntC<-1>{}, [&](auto m_tag) {
+            constexpr int m = decltype(m_tag)::value;
+            constexpr int q = m / 2;
+            if constexpr ((m & 1) == 0 && q < FM)
+                cA[q] = *(const u32x4*)(cb1 + aoff0 + 2048 * q);
+            else if constexpr ((m & 1) == 0 && q < FM + FN)
+                cW[q - FM] = *(const u32x4*)(cb1 + woff0 + 2048 * (q - FM));
+            if constexpr ((m & 1) == 1 && q < FM)
+                nA[q] = *(const u32x2*)(sb1 + 16 * (ra + 32 * q));
+            else if constexpr ((m & 1) == 1 && q < FM + FN)
+                nW[q - FM] = *(const u32x2*)(sb1 + 16 * (rw + 32 * (q - FM)));
+            if constexpr (m == CPS)
+                issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(0)>{}, IntC<RT_CK(1)>{});
+            if constexpr (m == CPS + 1 && (T & 1))
+                issue_scales((G + 3) >> 1, IntC<(((T + 3) >> 1) & 1)>{});
+        });
+        if constexpr (2 * (FM + FN) > NM) {
+            // rows left over when a k-step has fewer slots than reads
+#pragma unroll
+            for (int q = NM / 2; q < FM + FN; q++) {
+                if (q < FM) {
+                    cA[q] = *(const u32x4*)(cb1 + aoff0 + 2048 * q);
+                    nA[q] = *(const u32x2*)(sb1 + 16 * (ra + 32 * q));
+                } else {
+                    cW[q - FM] = *(const u32x4*)(cb1 + woff0 + 2048 * (q - FM));
+                    nW[q - FM] = *(const u32x2*)(sb1 + 16 * (rw + 32 * (q - FM)));
+                }
+            }
+        }
+        kstep(IntC<1>{}, IntC<6>{}, IntC<-1>{}, [&](auto m_tag) {
+            if constexpr (decltype(m_tag)::value == CPS)
+                issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(1)>{}, IntC<RT_CK(2)>{});
+        });
+        kstep(IntC<0>{}, IntC<7>{}, IntC<-1>{}, [&](auto m_tag) {
+            if constexpr (decltype(m_tag)::value == CPS)
+                issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(2)>{}, IntC<RT_CK(3)>{});
+        });
+        // k-step 7 decodes k-step 0 of group G + 1 (past the end: unused)
+        kstep(IntC<1>{}, IntC<0>{}, IntC<0>{}, [&](auto m_tag) {
+            if constexpr (decltype(m_tag)::value == CPS)
+                issue_codes(G + 3, IntC<(T + 3) & 3>{}, IntC<RT_CK(3)>{}, IntC<NH>{});
+        });
 #undef RT_CK
 #pragma unroll
         for (int i = 0; i < FM; i++)
@@ -1254,6 +1336,7 @@ gemm_rtile_kernel(GemmArgs p)
         for (int j = 0; j < FN; j++)
             sW[j] = nW[j];
     };
+    (void)none;
     int64_t G = 0;
     for (; G + 4 <= ngr; G += 4) {
         group(G, IntC<0>{});
