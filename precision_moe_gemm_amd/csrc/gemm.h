@@ -147,9 +147,11 @@ NVFP4_DEV void static_for(F&& f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// g * sigmoid(g) in fp32 with the hardware exponential and reciprocal
+// (about 1 ulp each, far below the bf16 rounding of h that follows)
 NVFP4_DEV float silu_f(float g)
 {
-    return g / (1.0f + __expf(-g));
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 // Output tile of a prefill-class workgroup: expert, A-side rows
@@ -954,6 +956,168 @@ gemm_tile_kernel(GemmArgs p)
     store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane, &lds_f[0][0]);
 }
 
+// Epilogue of gemm_rtile_kernel, whose MFMAs take the W fragment as the
+// first operand: acc[i][j] is the transposed 32x32 fragment, lane l holding
+// output row 32 i + l % 32 of the wave tile and, in element 4 q + t, output
+// column 32 j + 8 q + 4 (l / 32) + t.  Each pass stages 128 bytes of every
+// wave row in this wave's own LDS region (TM rows; 16-byte slot s of row r at
+// slot s ^ (r % 8)) and writes whole 16-byte pieces: 8 lanes per row, 8 rows
+// per store instruction.
+template <int BN, int TM, int TN, int FM, int FN, int MODE>
+NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float16_t (&acc)[FM][FN], int wave_m,
+                            int wave_n, int lane, uint8_t* stg)
+{
+    const float gscale = *p.a_global * p.w_global[tc.e];
+    const int mrow = lane & 31, g = lane >> 5;
+    const int64_t wrow0 = tc.row_begin + wave_m * TM;  // first output row of this wave
+    const int rows_left = (int)(tc.row_end - wrow0);
+    const int64_t N = p.N;
+    auto slot = [&](int r, int s) { return stg + r * 128 + 16 * (s ^ (r & 7)); };
+    const int rl = lane >> 3, sl = lane & 7;  // read-back: row 8 k + rl, slot sl
+    auto staged = [&]() {
+        // LDS operations of a wave complete in order; the fence keeps the
+        // compiler from moving the reads of other lanes' data above the writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    if constexpr (MODE == kModeGateUp) {
+        // h = silu(gate) * up, bf16: TN / 2 = 64 columns (128 bytes) per row
+        static_assert(TN / 2 * 2 == 128, "one pass holds the wave's h columns");
+        const int64_t hcol0 = tc.nt * (BN / 2) + wave_n * (TN / 2);
+        uint32_t hmax = 0;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const bool rv = 32 * i + mrow < rows_left;
+#pragma unroll
+            for (int j = 0; j < FN / 2; j++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        const float gg = acc[i][j][4 * q + t] * gscale;
+                        const float uu = acc[i][j + FN / 2][4 * q + t] * gscale;
+                        hb[t] = f32_to_bf16(silu_f(gg) * uu);
+                        const uint32_t mag = rv ? (hb[t] & 0x7FFFu) : 0u;
+                        hmax = hmax > mag ? hmax : mag;
+                    }
+                    // columns 32 j + 8 q + 4 g + t: bytes 64 j + 16 q + 8 g
+                    *(u32x2*)(slot(32 * i + mrow, 4 * j + q) + 8 * g) = (u32x2){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+                }
+            }
+        }
+        staged();
+        if (p.hq_global) {
+            // h straight to NVFP4: each lane encodes whole 16-element blocks
+            // (row b / 4, columns 16 (b % 4)) as the quantize kernel does
+            const float Gh = *p.hq_global, six = 6.0f * Gh;
+            for (int b = lane; b < TM * 4; b += 64) {
+                const int r = b >> 2, c16 = b & 3;
+                if (r < rows_left) {
+                    const u32x4 v0 = *(const u32x4*)slot(r, 2 * c16);
+                    const u32x4 v1 = *(const u32x4*)slot(r, 2 * c16 + 1);
+                    const uint32_t a0 = absmax_bits8(v0), a1 = absmax_bits8(v1);
+                    uint32_t sc;
+                    const float rcp = block_scale(a0 > a1 ? a0 : a1, Gh, six, &sc);
+                    const int64_t grow = wrow0 + r, col = hcol0 + 16 * c16;
+                    *(u32x2*)(p.hq_packed + grow * (N / 2) + col / 2) =
+                        (u32x2){encode_half(v0, rcp), encode_half(v1, rcp)};
+                    p.hq_scales[grow * (N / 16) + col / 16] = (uint8_t)sc;
+                }
+            }
+        } else {
+            uint16_t* h = (uint16_t*)p.out;
+#pragma unroll
+            for (int k = 0; k < TM / 8; k++) {
+                const int r = 8 * k + rl;
+                if (r < rows_left)
+                    *(u32x4*)(h + (wrow0 + r) * N + hcol0 + 8 * sl) = *(const u32x4*)slot(r, sl);
+            }
+            hmax = wave_max_u32(hmax);
+            if (lane == 0 && hmax != 0)
+                atomicMax(p.h_amax, hmax << 16);
+        }
+    } else {
+        const bool bf16_out = MODE == kModeDense && p.out_bf16;
+        const int64_t colw = tc.nt * BN + wave_n * TN;  // first output column of the wave
+        if (bf16_out) {
+            // passes over pairs of W fragments: 64 columns = 128 bytes per row
+            const bool vec = N % 8 == 0 && ((uintptr_t)p.out & 15) == 0;
+            uint16_t* ob = (uint16_t*)p.out;
+#pragma unroll
+            for (int jp = 0; jp < FN / 2; jp++) {
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int jj = 0; jj < 2; jj++)
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const float16_t& a = acc[i][2 * jp + jj];
+                            const uint32_t b0 = f32_to_bf16(a[4 * q] * gscale), b1 = f32_to_bf16(a[4 * q + 1] * gscale);
+                            const uint32_t b2 = f32_to_bf16(a[4 * q + 2] * gscale), b3 = f32_to_bf16(a[4 * q + 3] * gscale);
+                            *(u32x2*)(slot(32 * i + mrow, 4 * jj + q) + 8 * g) = (u32x2){b0 | (b1 << 16), b2 | (b3 << 16)};
+                        }
+                staged();
+#pragma unroll
+                for (int k = 0; k < TM / 8; k++) {
+                    const int r = 8 * k + rl;
+                    const int64_t col = colw + 64 * jp + 8 * sl;
+                    if (r < rows_left && col < N) {
+                        const u32x4 v = *(const u32x4*)slot(r, sl);
+                        uint16_t* dst = ob + (wrow0 + r) * N + col;
+                        if (vec) {
+                            *(u32x4*)dst = v;
+                        } else {
+                            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                            for (int t = 0; t < 8; t++)
+                                if (col + t < N)
+                                    dst[t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+                        }
+                    }
+                }
+                staged();
+            }
+        } else {
+            // fp32: one pass per W fragment, 32 columns = 128 bytes per row
+            const bool vec = N % 4 == 0 && ((uintptr_t)p.out & 15) == 0;
+            float* of = (float*)p.out;
+#pragma unroll
+            for (int j = 0; j < FN; j++) {
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const float16_t& a = acc[i][j];
+                        *(float4_t*)slot(32 * i + mrow, 2 * q + g) =
+                            (float4_t){a[4 * q] * gscale, a[4 * q + 1] * gscale, a[4 * q + 2] * gscale,
+                                       a[4 * q + 3] * gscale};
+                    }
+                staged();
+#pragma unroll
+                for (int k = 0; k < TM / 8; k++) {
+                    const int r = 8 * k + rl;
+                    const int64_t col = colw + 32 * j + 4 * sl;
+                    if (r < rows_left && col < N) {
+                        const float4_t v = *(const float4_t*)slot(r, sl);
+                        float* dst = of + (wrow0 + r) * N + col;
+                        if (vec) {
+                            *(float4_t*)dst = v;
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; t++)
+                                if (col + t < N)
+                                    dst[t] = v[t];
+                        }
+                    }
+                }
+                staged();
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill mainloop with register decode (K a multiple of 256).
 //
@@ -1011,7 +1175,6 @@ gemm_rtile_kernel(GemmArgs p)
     constexpr int CB = SROWS * kTGRow;                     // bytes per code buffer
     static_assert(BM % 64 == 0 && BN % 64 == 0 && NJ % 2 == 0, "tile shape");
     static_assert(MODE != kModeGateUp || FN % 2 == 0, "gate_up pairs gate and up fragments");
-    static_assert(TM * (BN / 2) * 2 <= CB, "an h pass of the epilogue fits one code buffer");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds_c0[CB];
     __shared__ __attribute__((aligned(16))) uint8_t lds_c1[CB];
@@ -1191,7 +1354,7 @@ gemm_rtile_kernel(GemmArgs p)
         static_for<NM>([&](auto m_tag) {
             constexpr int m = decltype(m_tag)::value;
             constexpr int i = m / FN, j = m % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(operand(oa[S][i]), operand(ow[S][j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(operand(ow[S][j]), operand(oa[S][i]), acc[i][j], 0, 0, 0);
             static_for<(m + 1) * NU / NM - m * NU / NM>([&](auto k_tag) {
                 constexpr int U = m * NU / NM + decltype(k_tag)::value;
                 if constexpr (PH >= 0 && (U & 1) == 0) {
@@ -1348,10 +1511,13 @@ gemm_rtile_kernel(GemmArgs p)
         group(G, IntC<0>{});
         group(G + 1, IntC<1>{});
     }
-    // copies past the end are still in flight into the buffers
+    // copies past the end are still in flight into the buffers; after the
+    // barrier every wave stages its output in its own part of two buffers
     wait_vm<0>();
     __syncthreads();
-    store_tile<BN, WM, WN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane, lds_c0);
+    static_assert(2 * TM * 128 <= CB, "two waves' output staging fits one code buffer");
+    store_tile_t<BN, TM, TN, FM, FN, MODE>(p, tc, acc, wave_m, wave_n, lane,
+                                           (wave < 2 ? lds_c0 : lds_c1) + (wave & 1) * TM * 128);
 }
 
 }  // namespace nvfp4
