@@ -1371,14 +1371,14 @@ gemm_rtile_kernel(GemmArgs p)
     };
     auto none = [](auto) {};
 
-    // ---- prologue: groups 0 and 1 and scale pair 0 staged, group 0 read,
-    // the first half of the copies of group 2 and scale pair 1 issued, the
-    // operands of k-step 0 decoded
+    // ---- prologue: group 0 and scale pair 0 staged (group 1 in flight),
+    // group 0 read, the first half of the copies of group 2 and scale pair 1
+    // issued, the operands of k-step 0 decoded
     issue_codes(0, IntC<0>{}, IntC<0>{}, IntC<NJ>{});
-    issue_codes(1, IntC<1>{}, IntC<0>{}, IntC<NJ>{});
     issue_scales(0, IntC<0>{});
-    wait_vm<0>();
-    __syncthreads();
+    issue_codes(1, IntC<1>{}, IntC<0>{}, IntC<NJ>{});
+    wait_vm<NJ>();  // group 0 and scale pair 0 (group 1 is awaited at the first barrier)
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < FM; i++)
         cA[i] = *(const u32x4*)(lds_c0 + aoff0 + 2048 * i);
