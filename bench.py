@@ -163,9 +163,10 @@ def main():
         "bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(gu_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
         "kernel": "grouped gate_up GEMM + SwiGLU, one nvfp4_moe_gate_up call: tile plan, then "
-                  "256-row and 128-row gemm_tile_kernel classes (f16 MFMA 32x32x16, codes staged "
-                  "by LDS DMA) and the 16-row gemm_stream_kernel class (f16 MFMA 16x16x32); "
-                  "power-of-two weight-scale variants (MXFP4-origin experts)",
+                  "256-row and 128-row gemm_rtile_kernel classes (codes staged by LDS DMA, "
+                  "decoded by each wave into f16 MFMA 32x32x16 operands) and the 16-row "
+                  "gemm_stream_kernel class (f16 MFMA 16x16x32); power-of-two weight-scale "
+                  "variants (MXFP4-origin experts)",
         "launch_ms": round(gu_ms, 4),
         "algorithmic_flops_per_launch": gu_flops,
         "frac_of_fp8_peak": round(gu_tflops / PEAK_FP8_TFLOPS, 4),
