@@ -14,8 +14,10 @@ audit) that only call the C functions.  bf16 tensors are passed as numpy
 Sources: the pages "Qwen3.8-Flash-Next-NVFP4" (section 核心: two-level scaling,
 4.5 bits, dynamic activations; section 证据链: scale audit),
 "DeepSeek-V4.1-Flash-NVFP4" (section 二: E2M1 table, packing, MXFP4 vs NVFP4;
-sections 一/四/六: lossless remap), "Qwen3.8-2.4T-A95B-NVFP4" (NVFP4 KV cache)
-and "Qwen3.8-27B-NVFP4" (section 2: NVFP4 MLP shapes).
+sections 一/四/六: lossless remap), "Qwen3.8-2.4T-A95B-NVFP4" (NVFP4 KV cache),
+"Qwen3.8-27B-NVFP4" (section 2: NVFP4 MLP shapes) and
+"Qwen3.8-Flash-Next-FP4-Local" (section 2.1: NVFP4 n-gram table; section 3.2:
+W4A16 NVFP4 MTP experts).
 """
 from __future__ import annotations
 
@@ -84,6 +86,9 @@ def _load():
             "orc_moe_gate_up": (ctypes.c_int, [P, P, f32, P, P, i32, i32, P, P, P, i64, i64, P, i64, P]),
             "orc_moe_down": (ctypes.c_int, [P, P, f32, P, i32, P, P, P, i64, i64, P, i64, P]),
             "orc_moe_combine": (ctypes.c_int, [P, P, P, i64, i32, i64, P]),
+            "orc_gemm_w4a16_rows": (ctypes.c_int, [P, i64, P, i64, P, P, f32, P, i64, i64, P]),
+            "orc_moe_w4a16_gate_up": (ctypes.c_int, [P, P, P, i32, i32, P, P, P, i64, i64, P, i64, P]),
+            "orc_moe_w4a16_down": (ctypes.c_int, [P, P, i32, P, P, P, i64, i64, P, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -237,6 +242,22 @@ def gemm(A: NVFP4, W: NVFP4) -> np.ndarray:
     return gemm_rows(A, W)
 
 
+def gemm_w4a16(a: np.ndarray, W: NVFP4, a_rows=None, w_rows=None) -> np.ndarray:
+    """W4A16 C = Gw * a[a_rows] @ deq0(W[w_rows])^T as float64 (a: bf16 bits
+    [M, K]; see orc_gemm_w4a16_rows)."""
+    a = np.ascontiguousarray(_u16(a))
+    M, K = a.shape
+    N, K2 = W.shape
+    assert K == K2
+    a_rows = np.arange(M, dtype=np.int64) if a_rows is None else np.ascontiguousarray(a_rows, np.int64)
+    w_rows = np.arange(N, dtype=np.int64) if w_rows is None else np.ascontiguousarray(w_rows, np.int64)
+    C = np.zeros((a_rows.size, w_rows.size), np.float64)
+    rc = _load().orc_gemm_w4a16_rows(_p(a), K, _p(a_rows), a_rows.size, _p(W.packed), _p(W.scales),
+                                     float(W.G), _p(w_rows), w_rows.size, K, _p(C))
+    _check(rc, "gemm_w4a16")
+    return C
+
+
 # --------------------------------------------------------------------------
 # MXFP4
 # --------------------------------------------------------------------------
@@ -364,6 +385,51 @@ def moe_forward(x: np.ndarray, ids: np.ndarray, w: np.ndarray, w13: Experts, w2:
     y = moe_down(hq, offsets, w2, rows)
     out = moe_combine(y, inv, w)
     return dict(xq=xq, perm=perm, offsets=offsets, inv=inv, h=h, hq=hq, y=y, out=out)
+
+
+def moe_w4a16_gate_up(x: np.ndarray, perm, offsets, k: int, w13: Experts, rows) -> np.ndarray:
+    """W4A16 h (bf16 bits) [len(rows), I] from the bf16 rows of x (see
+    orc_moe_w4a16_gate_up)."""
+    x = np.ascontiguousarray(_u16(x))
+    E = w13.G.size
+    twoI, H = w13.packed.shape[1], w13.packed.shape[2] * 2
+    I = twoI // 2
+    rows = np.ascontiguousarray(rows, np.int64)
+    h = np.zeros((rows.size, I), np.uint16)
+    _check(_load().orc_moe_w4a16_gate_up(_p(x), _p(np.ascontiguousarray(perm, np.int32)),
+                                         _p(np.ascontiguousarray(offsets, np.int32)), k, E, _p(w13.packed),
+                                         _p(w13.scales), _p(w13.G), H, I, _p(rows), rows.size, _p(h)),
+           "moe_w4a16_gate_up")
+    return h
+
+
+def moe_w4a16_down(h: np.ndarray, offsets, w2: Experts, rows) -> np.ndarray:
+    """W4A16 y (float64) [len(rows), H] from bf16 h rows in list order."""
+    h = np.ascontiguousarray(_u16(h))
+    E = w2.G.size
+    H, I = w2.packed.shape[1], w2.packed.shape[2] * 2
+    rows = np.ascontiguousarray(rows, np.int64)
+    y = np.zeros((rows.size, H), np.float64)
+    _check(_load().orc_moe_w4a16_down(_p(h), _p(np.ascontiguousarray(offsets, np.int32)), E, _p(w2.packed),
+                                      _p(w2.scales), _p(w2.G), H, I, _p(rows), rows.size, _p(y)),
+           "moe_w4a16_down")
+    return y
+
+
+def moe_w4a16_forward(x: np.ndarray, ids: np.ndarray, w: np.ndarray, w13: Experts, w2: Experts):
+    """W4A16 routed-expert MoE forward on bf16 x [T, H] ("Qwen3.8-Flash-Next-
+    FP4-Local", section 3.2): route -> gate_up + SwiGLU from the bf16 x rows
+    -> down from the bf16 h rows -> router-weighted combine.  No activation
+    is quantized.  Returns a dict of the intermediates (perm, offsets, inv,
+    h, y, out)."""
+    E = w13.G.size
+    T, k = ids.shape
+    perm, offsets, inv = moe_route(ids, E)
+    rows = np.arange(T * k, dtype=np.int64)
+    h = moe_w4a16_gate_up(x, perm, offsets, k, w13, rows)
+    y = moe_w4a16_down(h, offsets, w2, rows)
+    out = moe_combine(y, inv, w)
+    return dict(perm=perm, offsets=offsets, inv=inv, h=h, y=y, out=out)
 
 
 # --------------------------------------------------------------------------

@@ -16,6 +16,8 @@
  *   [A95B]       "Qwen3.8-2.4T-A95B-NVFP4" (NVFP4 KV cache, 4 KV heads x 256).
  *   [27B]        "Qwen3.8-27B-NVFP4", section 2 (NVFP4 MLP, hidden 5120 /
  *                intermediate 17408; weight / weight_scale / weight_scale_2).
+ *   [Local]      "Qwen3.8-Flash-Next-FP4-Local", section 3.2 (W4A16 NVFP4
+ *                MTP experts: NVFP4 weights, BF16 activations).
  *
  * Arithmetic rules.  Every float operation is one IEEE binary32 operation,
  * correctly rounded to nearest-even; the file must be built with
@@ -656,4 +658,137 @@ int orc_moe_combine(const double* y, const int32_t* inv, const float* w,
             out[t * H + n] = orc_bf16_from_double(acc);
         }
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W4A16: bf16 activations x NVFP4 weights                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Dequantized weight element without its global, as a double (exact). */
+static double deq0_value(const uint8_t* packed, const uint8_t* scales, int64_t row, int64_t K, int64_t k)
+{
+    uint8_t byte = packed[row * (K / 2) + k / 2];
+    uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
+    return orc_e2m1_value(nib) * orc_e4m3_value(scales[row * (K / 16) + k / 16]);
+}
+
+/*
+ * W4A16 product ("Qwen3.8-Flash-Next-FP4-Local", section 3.2: NVFP4 weights,
+ * BF16 activations):
+ *   C[i, j] = Gw * sum_k A[a_rows[i], k] * deq0(W[w_rows[j], k])
+ * A: bf16 bits, row stride lda.  Every product is exact in double (8 + 6
+ * significant bits); the sum is a compensated (Neumaier) double sum, within
+ * a few ulps of the exact sum, then multiplied by Gw.  C is [n_a, n_w].
+ */
+int orc_gemm_w4a16_rows(const uint16_t* A, int64_t lda, const int64_t* a_rows, int64_t n_a,
+                        const uint8_t* Wp, const uint8_t* Ws, float Gw,
+                        const int64_t* w_rows, int64_t n_w, int64_t K, double* C)
+{
+    int64_t i, j, k;
+    double* wv;
+    if (K % 16 != 0 || lda < K)
+        return ORC_SHAPE;
+    wv = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * (size_t)(n_w > 0 ? n_w : 1));
+    if (!wv)
+        return ORC_INVALID;
+    for (j = 0; j < n_w; j++)
+        for (k = 0; k < K; k++)
+            wv[j * K + k] = deq0_value(Wp, Ws, w_rows[j], K, k);
+    for (i = 0; i < n_a; i++) {
+        const uint16_t* a = A + a_rows[i] * lda;
+        for (j = 0; j < n_w; j++) {
+            double sum = 0.0, comp = 0.0;
+            for (k = 0; k < K; k++) {
+                double p = (double)bf16_to_float(a[k]) * wv[j * K + k];
+                double t = sum + p;
+                if (fabs(sum) >= fabs(p))
+                    comp += (sum - t) + p;
+                else
+                    comp += (p - t) + sum;
+                sum = t;
+            }
+            C[i * n_w + j] = (sum + comp) * (double)Gw;
+        }
+    }
+    free(wv);
+    return ORC_OK;
+}
+
+/*
+ * W4A16 gate_up + SwiGLU for listed pairs: as orc_moe_gate_up with the
+ * token's bf16 row x[perm[q] / k] in place of its NVFP4 row.  x: [T, H]
+ * bf16 bits.  h_out: [n_rows, I] bf16 bits.
+ */
+int orc_moe_w4a16_gate_up(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int32_t k,
+                          int32_t E, const uint8_t* w13p, const uint8_t* w13s, const float* G13,
+                          int64_t H, int64_t I, const int64_t* rows, int64_t n_rows, uint16_t* h_out)
+{
+    int64_t i, n, *w_rows, a_row;
+    double* gu;
+    int rc = ORC_OK;
+    if (H % 16 != 0)
+        return ORC_SHAPE;
+    w_rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * I));
+    gu = (double*)malloc(sizeof(double) * (size_t)(2 * I));
+    if (!w_rows || !gu) {
+        free(w_rows);
+        free(gu);
+        return ORC_INVALID;
+    }
+    for (n = 0; n < 2 * I; n++)
+        w_rows[n] = n;
+    for (i = 0; i < n_rows && rc == ORC_OK; i++) {
+        int64_t q = rows[i];
+        int32_t e = 0;
+        while (e < E && !(offsets[e] <= q && q < offsets[e + 1]))
+            e++;
+        if (e == E) {
+            rc = ORC_RANGE;
+            break;
+        }
+        a_row = perm[q] / k;
+        rc = orc_gemm_w4a16_rows(x, H, &a_row, 1, w13p + (size_t)e * (size_t)(2 * I) * (size_t)(H / 2),
+                                 w13s + (size_t)e * (size_t)(2 * I) * (size_t)(H / 16), G13[e], w_rows, 2 * I,
+                                 H, gu);
+        for (n = 0; n < I; n++)
+            h_out[i * I + n] = orc_bf16_from_double(silu(gu[n]) * gu[I + n]);
+    }
+    free(w_rows);
+    free(gu);
+    return rc;
+}
+
+/*
+ * W4A16 down projection for listed pairs: y[i] = W4A16 row product of the
+ * bf16 h row rows[i] (h in list order, [T*k, I]) with W2[e].  y_out:
+ * [n_rows, H] double.
+ */
+int orc_moe_w4a16_down(const uint16_t* h, const int32_t* offsets, int32_t E, const uint8_t* w2p,
+                       const uint8_t* w2s, const float* G2, int64_t H, int64_t I, const int64_t* rows,
+                       int64_t n_rows, double* y_out)
+{
+    int64_t i, n, *w_rows;
+    int rc = ORC_OK;
+    if (I % 16 != 0)
+        return ORC_SHAPE;
+    w_rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)H);
+    if (!w_rows)
+        return ORC_INVALID;
+    for (n = 0; n < H; n++)
+        w_rows[n] = n;
+    for (i = 0; i < n_rows && rc == ORC_OK; i++) {
+        int64_t q = rows[i];
+        int32_t e = 0;
+        while (e < E && !(offsets[e] <= q && q < offsets[e + 1]))
+            e++;
+        if (e == E) {
+            rc = ORC_RANGE;
+            break;
+        }
+        rc = orc_gemm_w4a16_rows(h, I, &q, 1, w2p + (size_t)e * (size_t)H * (size_t)(I / 2),
+                                 w2s + (size_t)e * (size_t)H * (size_t)(I / 16), G2[e], w_rows, H, I,
+                                 y_out + i * H);
+    }
+    free(w_rows);
+    return rc;
 }
