@@ -373,6 +373,12 @@ def breakdown(args):
     ms = time_loop(f, it, st)
     res["moe_384e_top8_decode_T64_static_globals"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
                                                       "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
+    # the same experts as W4A16 (bf16 activations, no activation quantization)
+    f = lambda: nv.nvfp4_moe_w4a16(x, ids, wt, W.w13, W.w2, out=out, ws=ws)
+    f()
+    ms = time_loop(f, it, st)
+    res["moe_384e_top8_w4a16_decode_T64"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
+                                             "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
     p13, s13 = W.mx13
     dst = nv.NVFP4Tensor.empty(2 * c4.I, c4.H, c4.E, dev)
     rws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_REMAP, c4.E, 0, 0, 2 * c4.I, c4.H), dtype=torch.uint8, device=dev)

@@ -197,6 +197,37 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * W4A16 GEMM (page "Qwen3.8-Flash-Next-FP4-Local", section 3.2: routed
+ * experts of the MTP head keep their activations in BF16 and only the
+ * weights in NVFP4):
+ *   C[m, n] = G_W * sum_k A[m, k] * (e2m1*s)(W[n, k])
+ * A: bf16 [M, K] with row stride lda (elements, lda >= K, lda % 8 == 0,
+ * 16-byte aligned); W: [N, K] (batch 1); C: [M, N] row-major, fp32 or bf16.
+ * The weights are decoded exactly to bf16 and multiplied on the bf16 MFMA
+ * path: products are exact, the sum is accumulated in fp32.  Every M runs
+ * the weight-streaming kernel (16 rows of A per tile): the format serves
+ * decode-sized batches.  K % 256 == 0 on this build (else
+ * NVFP4_ERR_UNSUPPORTED).  ws: as nvfp4_gemm (nvfp4_workspace_size
+ * (NVFP4_OP_GEMM, M, 0, 0, K, N) bytes, or NULL).
+ */
+nvfp4_status nvfp4_gemm_w4a16(const void* a_bf16, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
+                              void* C, nvfp4_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * W4A16 routed-expert MoE layer (page "Qwen3.8-Flash-Next-FP4-Local",
+ * section 3.2: W4A16_NVFP4 MTP experts): as nvfp4_moe_grouped_gemm without
+ * the activation quantization: route, gate_up from the bf16 rows of x
+ * (g || u = x[t] W13[e]^T, h = silu(g) * u rounded to bf16), down from the
+ * bf16 h rows (y = h W2[e]^T, fp32), combine out[t] = sum_j topk_w[t, j]
+ * y[t, j] (j in order) rounded to bf16.  Arguments and ws as
+ * nvfp4_moe_grouped_gemm (nvfp4_workspace_size(NVFP4_OP_MOE, ...)).
+ * H % 256 == 0 and I % 256 == 0 on this build (else NVFP4_ERR_UNSUPPORTED).
+ */
+nvfp4_status nvfp4_moe_w4a16(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, int64_t T,
+                             int32_t k, int32_t E, const nvfp4_tensor* w13, const nvfp4_tensor* w2,
+                             void* out_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Routed-expert MoE layer with NVFP4 experts (page "Qwen3.8-Flash-Next-NVFP4":
  * routed experts with fused gate_up / down projections, top-k routing; page
  * "DeepSeek-V4.1-Flash-NVFP4", section 三: experts w1, w3, w2):

@@ -22,7 +22,7 @@ __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
-    "nvfp4_gather_dequantize",
+    "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
     "nvfp4_recipe", "status_string",
 ]
@@ -214,6 +214,46 @@ def nvfp4_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torc
         _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, E, ctypes.byref(c13), ctypes.byref(c2),
         _ptr(static_in_globals), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
         "nvfp4_moe_grouped_gemm")
+    return out
+
+
+def nvfp4_gemm_w4a16(a: torch.Tensor, W: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None):
+    """C[M, N] = a W^T with bf16 activations a [M, K] (row stride a.stride(0))
+    and NVFP4 weights W [N, K]."""
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16 or a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be a 2-D bf16 tensor with unit column stride")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, W.rows), dtype=dtype, device=a.device)
+    code = _lib.BF16 if out.dtype == torch.bfloat16 else _lib.F32
+    if ws is None:
+        n = nvfp4_workspace_size(_lib.OP_GEMM, M, 0, 0, K, W.rows)
+        ws = _workspace(n, a.device) if n else None
+    wc = W.c()
+    _check(_lib.load().nvfp4_gemm_w4a16(_ptr(a), M, K, a.stride(0), ctypes.byref(wc), _ptr(out), code, _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(a.device)), "nvfp4_gemm_w4a16")
+    return out
+
+
+def nvfp4_moe_w4a16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13: NVFP4Tensor,
+                    w2: NVFP4Tensor, out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """W4A16 routed-expert MoE forward: bf16 x [T, H] -> bf16 [T, H], no
+    activation quantization."""
+    _need_cuda(x, topk_ids, topk_w)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E = w13.batch
+    I = w13.rows // 2
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE, T, k, E, H, I), x.device)
+    c13, c2 = w13.c(), w2.c()
+    _check(_lib.load().nvfp4_moe_w4a16(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, E, ctypes.byref(c13), ctypes.byref(c2),
+        _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)), "nvfp4_moe_w4a16")
     return out
 
 

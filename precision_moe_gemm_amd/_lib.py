@@ -51,6 +51,8 @@ SIGNATURES = {
     "mxfp4_to_nvfp4": (ST, [P, P, I64, I64, I64, TP, P, SZ, P]),
     "nvfp4_gemm": (ST, [TP, TP, P, ctypes.c_int, P, SZ, P]),
     "nvfp4_moe_grouped_gemm": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, P, SZ, P]),
+    "nvfp4_gemm_w4a16": (ST, [P, I64, I64, I64, TP, P, ctypes.c_int, P, SZ, P]),
+    "nvfp4_moe_w4a16": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, SZ, P]),
     "nvfp4_moe_route": (ST, [P, I64, I32, I32, P, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up": (ST, [TP, P, P, I64, I32, I32, TP, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up_q": (ST, [TP, P, P, I64, I32, I32, TP, P, TP, P, SZ, P]),

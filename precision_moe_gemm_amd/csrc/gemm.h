@@ -80,6 +80,10 @@ struct GemmArgs {
     const float* hq_global;
     uint8_t* hq_packed;
     uint8_t* hq_scales;
+    // W4A16 (weight-streaming kernel only): the A operand is bf16 rows of
+    // `lda` elements instead of NVFP4 (a_packed / a_scales / a_global unused)
+    const uint16_t* a_bf16;
+    int64_t lda;
 };
 
 // 16-byte chunk slot of chunk c in tile row r (8 chunks per row).
@@ -114,6 +118,32 @@ NVFP4_DEV u32x4 decode_chunk_p2(uint32_t codes, float s)
     r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 1));
     r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 2));
     r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 3));
+    return r;
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// 8 codes times an fp32 block scale s into 8 bf16 (16 bytes): q -> fp32,
+// one multiply each (exact: q * s has at most 6 significant bits), bf16.
+NVFP4_DEV u32x4 decode_chunk_bf16(uint32_t codes, float s)
+{
+    const float2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const float2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const float2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const float2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    return (u32x4){pack_bf16x2(q0.x * s, q0.y * s), pack_bf16x2(q1.x * s, q1.y * s),
+                   pack_bf16x2(q2.x * s, q2.y * s), pack_bf16x2(q3.x * s, q3.y * s)};
+}
+
+// 8 codes times a power-of-two (or zero) scale s into 8 bf16: the
+// conversion applies 2^exponent(s) exactly.
+NVFP4_DEV u32x4 decode_chunk_bf16_p2(uint32_t codes, float s)
+{
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 3));
     return r;
 }
 
@@ -1556,7 +1586,7 @@ NVFP4_DEV int sk_wslot(int r, int c) { return c ^ ((r >> 1) & 7); }
 // 16-byte slot of f16 chunk c (of 32) in A tile row r
 NVFP4_DEV int sk_aslot(int r, int c) { return c ^ (r & 15); }
 
-template <int MODE, bool P2>
+template <int MODE, bool P2, bool A16>
 __global__ void __launch_bounds__(kSkThreads)
 gemm_stream_kernel(GemmArgs p)
 {
@@ -1646,14 +1676,24 @@ gemm_stream_kernel(GemmArgs p)
     const uint8_t* xsrc = loads_scales ? wsc + w_row_of(tid) * kpsb + st0 * (kSkBK / 16)
                                        : p.a_packed + ar * kpb + st0 * (kSkBK / 2) + 16 * pc;
     const uint8_t* ysrc = p.a_scales + ar * kpsb + st0 * (kSkBK / 16) + 2 * pc;
+    // W4A16: A row ar as bf16, this thread's 32 elements (64 bytes) of a stage
+    const uint16_t* bsrc = A16 ? p.a_bf16 + ar * p.lda + st0 * kSkBK + 32 * pc : nullptr;
 
     u32x4 wreg[3][4];
     u32x4 xreg[3];
     uint32_t yreg[3];
+    u32x4 breg[3][4];
     auto load_stage = [&](int64_t st, int set) {
-        const int64_t xo = loads_scales ? st * (kSkBK / 16) : st * (kSkBK / 2);
-        xreg[set] = *(const u32x4*)(xsrc + xo);
-        yreg[set] = *(const uint16_t*)(ysrc + st * (kSkBK / 16));
+        if (A16 && !loads_scales) {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                breg[set][i] = *(const u32x4*)(bsrc + st * kSkBK + 8 * i);
+        } else {
+            const int64_t xo = loads_scales ? st * (kSkBK / 16) : st * (kSkBK / 2);
+            xreg[set] = *(const u32x4*)(xsrc + xo);
+            if (!A16)
+                yreg[set] = *(const uint16_t*)(ysrc + st * (kSkBK / 16));
+        }
 #pragma unroll
         for (int j = 0; j < 4; j++)
             wreg[set][j] = *(const u32x4*)(wsrc[j] + st * (kSkBK / 2));
@@ -1665,6 +1705,11 @@ gemm_stream_kernel(GemmArgs p)
             *(u32x4*)(&lds_w[b][wdst[j]]) = wreg[set][j];
         if (loads_scales) {
             *(u32x4*)(&lds_ws[b][16 * tid]) = xreg[set];
+        } else if (A16) {
+            uint8_t* rowp = &lds_a[b][arow * kSkRowF16];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                *(u32x4*)(rowp + 16 * sk_aslot(arow, 4 * pc + i)) = breg[set][i];
         } else {
             const half2_t s2 = scales2<0>(yreg[set]);
             uint8_t* rowp = &lds_a[b][arow * kSkRowF16];
@@ -1701,15 +1746,26 @@ gemm_stream_kernel(GemmArgs p)
             }
 #pragma unroll
             for (int d = 0; d < 4; d++) {
-                const half8_t fa = *(const half8_t*)(ta + 16 * sk_aslot(fr, 16 * q + 4 * kg + d));
+                const u32x4 fa = *(const u32x4*)(ta + 16 * sk_aslot(fr, 16 * q + 4 * kg + d));
 #pragma unroll
                 for (int f = 0; f < 2; f++) {
                     const u32x4 pv = piece[f];
                     const uint32_t codes = d == 0 ? pv.x : d == 1 ? pv.y : d == 2 ? pv.z : pv.w;
-                    const u32x4 dv = P2 ? decode_chunk_p2(codes, sf[f][d >> 1])
-                                        : decode_chunk(codes, d < 2 ? s2[f].x : s2[f].y);
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, __builtin_bit_cast(half8_t, dv),
-                                                                    acc[f], 0, 0, 0);
+                    if constexpr (A16) {
+                        // bf16 operands; the scale as fp32 (general scales:
+                        // the fp8 byte pair converted exactly)
+                        const float sc = P2 ? sf[f][d >> 1] : (float)(d < 2 ? s2[f].x : s2[f].y);
+                        const u32x4 dv = P2 ? decode_chunk_bf16_p2(codes, sc) : decode_chunk_bf16(codes, sc);
+                        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa),
+                                                                         __builtin_bit_cast(bf16x8_t, dv), acc[f],
+                                                                         0, 0, 0);
+                    } else {
+                        const u32x4 dv = P2 ? decode_chunk_p2(codes, sf[f][d >> 1])
+                                            : decode_chunk(codes, d < 2 ? s2[f].x : s2[f].y);
+                        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, fa),
+                                                                        __builtin_bit_cast(half8_t, dv), acc[f],
+                                                                        0, 0, 0);
+                    }
                 }
             }
         }
@@ -1744,7 +1800,7 @@ gemm_stream_kernel(GemmArgs p)
 
     // ---- epilogue: lane holds output rows 4 kg + i, column fr of each
     // fragment ------------------------------------------------------------
-    const float gscale = *p.a_global * p.w_global[e];
+    const float gscale = (A16 ? 1.0f : *p.a_global) * p.w_global[e];
     const int rows_left = (int)(row_end - row_begin);
     if (MODE == kModeGateUp && p.ksplit > 1) {
         // K split: scaled partial gate and up sums to plane ks, rows of 2N

@@ -174,10 +174,14 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     blocks = ceil_div(blocks, 8) * 8;
     if (blocks > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    if (p.w_pow2)
-        gemm_stream_kernel<MODE, true><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    if (p.a_bf16 && p.w_pow2)
+        gemm_stream_kernel<MODE, true, true><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    else if (p.a_bf16)
+        gemm_stream_kernel<MODE, false, true><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    else if (p.w_pow2)
+        gemm_stream_kernel<MODE, true, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
     else
-        gemm_stream_kernel<MODE, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+        gemm_stream_kernel<MODE, false, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
     nvfp4_status s = launch_status();
     if (s != NVFP4_OK || p.ksplit <= 1 || MODE == kModeDown)
         return s;  // grouped down: the combine adds the planes
@@ -199,7 +203,8 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
 {
     if (p.ksplit < 1)
         p.ksplit = 1;
-    if (use_stream_gemm(p.M, p.K)) {
+    if (p.a_bf16 || use_stream_gemm(p.M, p.K)) {
+        // (W4A16 runs the weight-streaming kernel at every M)
         p.n_tiles = ceil_div(p.N, kSkBN);
         return launch_stream_gemm<kModeDense>(p, ceil_div(p.M, kSkBM), st);
     }
@@ -279,10 +284,12 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
 {
     const bool stream_ok = p.K % kSkBK == 0;
     const int small_bm = grouped_small_bm(p.K);
+    if (p.a_bf16 && !stream_ok)
+        return NVFP4_ERR_UNSUPPORTED;
     if (p.ksplit < 1 || !stream_ok)
         p.ksplit = 1;
-    if (p.ksplit > 1)
-        all_small = 1;  // the split planes cover every row
+    if (p.ksplit > 1 || p.a_bf16)
+        all_small = 1;  // the split planes cover every row; W4A16 streams every tile
     nvfp4_status s = NVFP4_OK;
     if (!plan_ready) {
         moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
@@ -666,6 +673,48 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
     return dispatch_dense(p, S(stream));
 }
 
+nvfp4_status nvfp4_gemm_w4a16(const void* a, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
+                              void* C, nvfp4_dtype dtype, void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = check_tensor(W);
+    if (s != NVFP4_OK)
+        return s;
+    if (!C || (dtype != NVFP4_F32 && dtype != NVFP4_BF16))
+        return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || K < 0 || lda < K || W->cols != K || W->batch != 1)
+        return NVFP4_ERR_SHAPE;
+    if (M == 0 || W->rows == 0)
+        return NVFP4_OK;
+    if (K == 0 || K % kSkBK != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (!a || !aligned(a, 16) || lda % 8 != 0)
+        return NVFP4_ERR_INVALID_ARG;
+    GemmArgs p{};
+    p.a_bf16 = (const uint16_t*)a;
+    p.lda = lda;
+    p.w_packed = W->packed;
+    p.w_scales = W->scales;
+    p.w_global = W->global;
+    p.w_pow2 = (W->flags & NVFP4_POW2_SCALES) != 0;
+    p.K = K;
+    p.M = M;
+    p.N = W->rows;
+    p.experts = 1;
+    p.out = C;
+    p.out_bf16 = dtype == NVFP4_BF16;
+    p.ksplit = 1;
+    const int ksplit = gemm_ksplit(p.M, p.N, p.K);
+    if (ksplit > 1 && ws) {
+        if (!aligned(ws, 256))
+            return NVFP4_ERR_INVALID_ARG;
+        if (ws_bytes < gemm_ws_bytes(p.M, p.N, p.K))
+            return NVFP4_ERR_WORKSPACE;
+        p.ksplit = ksplit;
+        p.partial = (float*)ws;
+    }
+    return dispatch_dense(p, S(stream));
+}
+
 nvfp4_status nvfp4_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
                              int32_t* offsets, int32_t* inv, void* ws, size_t ws_bytes, void* stream)
 {
@@ -914,6 +963,88 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     // 6. combine (adds the planes of y in order)
     if (!w || H % 8 != 0)
         return NVFP4_ERR_SHAPE;
+    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
+                                                                   (u32x2*)out);
+    return launch_status();
+}
+
+nvfp4_status nvfp4_moe_w4a16(const void* x, const int32_t* ids, const float* w, int64_t T, int32_t k,
+                             int32_t E, const nvfp4_tensor* w13, const nvfp4_tensor* w2, void* out, void* ws,
+                             size_t ws_bytes, void* stream)
+{
+    int64_t H = 0, I = 0;
+    nvfp4_status s = check_experts(w13, w2, E, &H, &I);
+    if (s != NVFP4_OK)
+        return s;
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    if (H % kSkBK != 0 || I % kSkBK != 0 || H % 8 != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (T == 0)
+        return NVFP4_OK;
+    if (!x || !ids || !w || !out || !ws || !aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    const MoeLayout L = moe_layout(T, k, E, H, I);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    hipStream_t st = S(stream);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    int32_t* offsets = at<int32_t>(ws, L.r.offsets);
+    uint32_t* hmax = at<uint32_t>(ws, L.hmax);
+    // 1. route; every tile of both projections is a 16-row streaming tile
+    const int ksplit = moe_down_ksplit(T, k, E, H, I);
+    const int gsplit = moe_gate_ksplit(T, k, E, H, I);
+    const bool small = T * k <= kRouteSmall;
+    if (small)
+        s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
+                       kSkBM, 1, at<int32_t>(ws, L.r.plan_dn), kSkBM, 1);
+    else
+        s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
+    if (s != NVFP4_OK)
+        return s;
+    // 2. gate_up + SwiGLU from the bf16 rows of x (h bf16, list order)
+    GemmArgs p{};
+    p.a_bf16 = (const uint16_t*)x;
+    p.lda = H;
+    p.w_packed = w13->packed;
+    p.w_scales = w13->scales;
+    p.w_global = w13->global;
+    p.w_pow2 = (w13->flags & NVFP4_POW2_SCALES) != 0;
+    p.K = H;
+    p.N = I;
+    p.M = T * k;
+    p.perm = perm;
+    p.topk = k;
+    p.experts = E;
+    p.out = at<void>(ws, L.h);
+    p.h_amax = hmax;
+    p.ksplit = gsplit;
+    p.partial = gsplit > 1 ? at<float>(ws, L.gpart) : nullptr;
+    s = dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, 1, at<int32_t>(ws, L.r.plan_gu), small, st);
+    if (s != NVFP4_OK)
+        return s;
+    // 3. down from the bf16 h rows (K split into planes of y for tiny batches)
+    float* y = at<float>(ws, L.y);
+    GemmArgs q{};
+    q.a_bf16 = at<const uint16_t>(ws, L.h);
+    q.lda = I;
+    q.w_packed = w2->packed;
+    q.w_scales = w2->scales;
+    q.w_global = w2->global;
+    q.w_pow2 = (w2->flags & NVFP4_POW2_SCALES) != 0;
+    q.K = I;
+    q.N = H;
+    q.M = T * k;
+    q.topk = k;
+    q.experts = E;
+    q.out = y;
+    q.ksplit = ksplit;
+    q.partial = y;
+    s = dispatch_grouped<kModeDown>(q, offsets, T * k, E, 1, at<int32_t>(ws, L.r.plan_dn), small, st);
+    if (s != NVFP4_OK)
+        return s;
+    // 4. combine (adds the planes of y in order)
     combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
                                                                    (u32x2*)out);
     return launch_status();
