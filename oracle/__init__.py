@@ -89,6 +89,8 @@ def _load():
             "orc_gemm_w4a16_rows": (ctypes.c_int, [P, i64, P, i64, P, P, f32, P, i64, i64, P]),
             "orc_moe_w4a16_gate_up": (ctypes.c_int, [P, P, P, i32, i32, P, P, P, i64, i64, P, i64, P]),
             "orc_moe_w4a16_down": (ctypes.c_int, [P, P, i32, P, P, P, i64, i64, P, i64, P]),
+            "orc_mxfp8_encode": (ctypes.c_int, [P, i64, i64, i64, P, P]),
+            "orc_mx_gemm_w4a8_rows": (ctypes.c_int, [P, P, P, i64, P, P, P, i64, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -294,6 +296,33 @@ def mxfp4_to_nvfp4(packed: np.ndarray, e8: np.ndarray) -> NVFP4:
     _check(_load().orc_mxfp4_to_nvfp4(_p(packed), _p(e8), R, K, _p(out_p), _p(out_s), _p(G)),
            "mxfp4_to_nvfp4")
     return NVFP4(out_p, out_s, G[0])
+
+
+def mxfp8_encode(x: np.ndarray):
+    """MXFP8 (E4M3, UE8M0 per 32) of bf16 bits [R, K] -> (codes [R, K], e8m0
+    [R, K/32]) (see orc_mxfp8_encode)."""
+    x = np.ascontiguousarray(_u16(x))
+    R, K = x.shape
+    q = np.zeros((R, K), np.uint8)
+    e8 = np.zeros((R, K // 32), np.uint8)
+    _check(_load().orc_mxfp8_encode(_p(x), R, K, K, _p(q), _p(e8)), "mxfp8_encode")
+    return q, e8
+
+
+def mx_gemm_w4a8(a: np.ndarray, a_e8: np.ndarray, w_packed: np.ndarray, w_e8: np.ndarray,
+                 a_rows=None, w_rows=None) -> np.ndarray:
+    """MX W4A8 C = A_mxfp8 @ W_mxfp4^T as float64 (see orc_mx_gemm_w4a8_rows)."""
+    a, a_e8 = np.ascontiguousarray(a, np.uint8), np.ascontiguousarray(a_e8, np.uint8)
+    w_packed, w_e8 = np.ascontiguousarray(w_packed, np.uint8), np.ascontiguousarray(w_e8, np.uint8)
+    M, K = a.shape
+    N = w_packed.shape[0]
+    assert w_packed.shape[1] * 2 == K
+    a_rows = np.arange(M, dtype=np.int64) if a_rows is None else np.ascontiguousarray(a_rows, np.int64)
+    w_rows = np.arange(N, dtype=np.int64) if w_rows is None else np.ascontiguousarray(w_rows, np.int64)
+    C = np.zeros((a_rows.size, w_rows.size), np.float64)
+    _check(_load().orc_mx_gemm_w4a8_rows(_p(a), _p(a_e8), _p(a_rows), a_rows.size, _p(w_packed), _p(w_e8),
+                                         _p(w_rows), w_rows.size, K, _p(C)), "mx_gemm_w4a8")
+    return C
 
 
 # --------------------------------------------------------------------------

@@ -792,3 +792,102 @@ int orc_moe_w4a16_down(const uint16_t* h, const int32_t* offsets, int32_t E, con
     free(w_rows);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* MX-native W4A8: MXFP8 activations x MXFP4 weights                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * MXFP8 encode of a bf16 matrix ([DSV41] §二: the reference FP8 x FP4 GEMM
+ * quantizes activations in blocks with power-of-two scales; the reading
+ * taken: blocks of 32 along the row, UE8M0 scale 2^e with e the smallest
+ * integer such that amax <= 448 * 2^e (no element saturates), clamped to
+ * [-127, 127], e = 0 for an all-zero block).  Element: the nearest E4M3
+ * magnitude to |x| * 2^-e (brute-force search, ties to the even code),
+ * sign bit = signbit(x).  out: [R, K] E4M3 bytes; e8m0: [R, K/32] (e + 127).
+ */
+int orc_mxfp8_encode(const uint16_t* x, int64_t R, int64_t K, int64_t ld, uint8_t* out, uint8_t* e8m0)
+{
+    int64_t r, b, j;
+    if (K % 32 != 0 || ld < K)
+        return ORC_SHAPE;
+    for (r = 0; r < R; r++)
+        for (b = 0; b < K / 32; b++) {
+            const uint16_t* xb = x + r * ld + 32 * b;
+            double amax = 0.0;
+            int e = 0;
+            for (j = 0; j < 32; j++) {
+                double a = fabs((double)bf16_to_float(xb[j]));
+                if (a > amax)
+                    amax = a;
+            }
+            if (amax > 0.0) {
+                e = -127;
+                while (e < 127 && amax > 448.0 * ldexp(1.0, e))
+                    e++;
+            }
+            e8m0[r * (K / 32) + b] = (uint8_t)(e + 127);
+            for (j = 0; j < 32; j++) {
+                float v = bf16_to_float(xb[j]);
+                float y = (float)ldexp(fabs((double)v), -e);
+                uint8_t c = orc_e4m3_encode(y);
+                out[r * K + 32 * b + j] = (uint8_t)(c | (signbit(v) ? 0x80 : 0));
+            }
+        }
+    return ORC_OK;
+}
+
+/* Value of an E8M0 byte (2^(b - 127)); byte 255 (NaN) is an error for the
+ * caller to avoid. */
+static double e8m0_pow(uint8_t b)
+{
+    return ldexp(1.0, (int)b - 127);
+}
+
+/*
+ * MX-native W4A8 product ([DSV41] §二: FP8 activations, MXFP4 weights, block
+ * scales applied inside the accumulation):
+ *   C[i, j] = sum over 32-blocks b of 2^(ea - 127) 2^(ew - 127)
+ *             * sum_{k in b} e4m3(A[a_rows[i], k]) * e2m1(W[w_rows[j], k])
+ * Each block sum is an exact int64 sum of the integer images
+ * (2^9 * e4m3) * (2 * e2m1), scaled exactly by 2^(ea + ew - 264); the block
+ * terms are added in double with compensated summation.  A: [.., K] E4M3
+ * with Ae [.., K/32]; W: packed [.., K/2] with We [.., K/32].  C: [n_a, n_w].
+ */
+int orc_mx_gemm_w4a8_rows(const uint8_t* A, const uint8_t* Ae, const int64_t* a_rows, int64_t n_a,
+                          const uint8_t* Wp, const uint8_t* We, const int64_t* w_rows, int64_t n_w, int64_t K,
+                          double* C)
+{
+    int64_t i, j, b, k;
+    if (K % 32 != 0)
+        return ORC_SHAPE;
+    for (i = 0; i < n_a; i++)
+        for (j = 0; j < n_w; j++) {
+            const uint8_t* a = A + a_rows[i] * K;
+            const uint8_t* w = Wp + w_rows[j] * (K / 2);
+            double sum = 0.0, comp = 0.0;
+            for (b = 0; b < K / 32; b++) {
+                uint8_t ea = Ae[a_rows[i] * (K / 32) + b], ew = We[w_rows[j] * (K / 32) + b];
+                int64_t acc = 0;
+                double t, p;
+                if (ea == 255 || ew == 255)
+                    return ORC_RANGE;
+                for (k = 32 * b; k < 32 * b + 32; k++) {
+                    uint8_t byte = w[k / 2];
+                    uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
+                    int64_t ai = (int64_t)ldexp(orc_e4m3_value(a[k]), 9);
+                    int64_t wi = (int64_t)(2.0 * orc_e2m1_value(nib));
+                    acc += ai * wi;
+                }
+                p = ldexp((double)acc, -10) * e8m0_pow(ea) * e8m0_pow(ew);
+                t = sum + p;
+                if (fabs(sum) >= fabs(p))
+                    comp += (sum - t) + p;
+                else
+                    comp += (p - t) + sum;
+                sum = t;
+            }
+            C[i * n_w + j] = sum + comp;
+        }
+    return ORC_OK;
+}

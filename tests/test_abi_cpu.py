@@ -18,7 +18,7 @@ def _declared():
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([a-z][a-z0-9_]*)\s*\(",
                        src, flags=re.M)
-    return sorted(set(n for n in names if n.startswith(("nvfp4_", "mxfp4_"))))
+    return sorted(set(n for n in names if n.startswith(("nvfp4_", "mxfp4_", "mxfp8_", "mx_"))))
 
 
 @pytest.fixture(scope="module")
