@@ -327,6 +327,29 @@ def breakdown(args):
     del mlp
     torch.cuda.empty_cache()
 
+    # MX-native W4A8 (MXFP8 activations x MXFP4 weights) on the 8192 x 4096 x
+    # 7168 GEMM, and the MXFP8 activation encode
+    log("breakdown: MX W4A8 GEMM")
+    Mm, Nm, Km = 8192, 4096, 7168
+    xa = synth.normal_bf16((Mm, Km), 1.0, (860, Mm, Km), dev)
+    wm = synth.normal_bf16((Nm, Km), 0.02, (861, Nm, Km), dev)
+    q8, q8e = nv.mxfp8_quantize(xa)
+    wp4, we4 = nv.mxfp4_quantize(wm)
+    del wm
+    cm = torch.empty((Mm, Nm), dtype=torch.bfloat16, device=dev)
+    f = lambda: nv.mx_gemm_w4a8(q8, q8e, wp4, we4, out=cm)
+    f()
+    ms = time_loop(f, it, st)
+    ms_q = time_loop(lambda: nv.mxfp8_quantize(xa), it, st)
+    tf = 2.0 * Mm * Nm * Km / ms / 1e9
+    res["mx_w4a8_gemm_8192x4096x7168"] = {
+        "ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+        "frac_f16_peak": round(tf / PEAK_F16_TFLOPS, 4),
+        "mxfp8_quantize_ms": round(ms_q, 4), "mxfp8_quantize_GBps": gbs(Mm * Km * (2 + 1 + 1 / 32), ms_q),
+        "quantize_bytes_basis": "2 B/elem bf16 read + 1 B E4M3 + 1/32 B scale written"}
+    del xa, q8, q8e, wp4, we4, cm
+    torch.cuda.empty_cache()
+
     # 512-expert top-10 MoE
     c3 = synth.C3
     log("breakdown: 512-expert MoE")

@@ -197,6 +197,39 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * MXFP8 activation encode for the MX-native W4A8 GEMM (page
+ * "DeepSeek-V4.1-Flash-NVFP4", section 二: the reference FP8 x FP4 GEMM
+ * quantizes activations in blocks with power-of-two scales).  Per block of
+ * 32 elements along a row: scale 2^e, e the smallest integer with
+ * amax <= 448 * 2^e (so no element saturates), clamped to [-127, 127]; an
+ * all-zero block takes e = 0.  Elements x * 2^-e rounded to E4M3 (nearest,
+ * ties to even; -0 keeps its sign).  x: bf16 [rows, cols] with row stride ld
+ * (elements, ld % 8 == 0, 16-byte aligned); fp8: E4M3 bytes [rows, cols]
+ * (16-byte aligned); e8m0: UE8M0 bytes [rows, cols / 32] (e + 127).
+ * cols % 32 == 0.  Inputs must be finite.
+ */
+nvfp4_status mxfp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, uint8_t* fp8,
+                            uint8_t* e8m0, void* stream);
+
+/*
+ * MX-native W4A8 GEMM (page "DeepSeek-V4.1-Flash-NVFP4", section 二: MXFP4
+ * weights, FP8 activations, the power-of-two block scales applied inside the
+ * accumulation; the routed experts are MXFP4 in the original checkpoint):
+ *   C[m, n] = sum over 32-element blocks b of K of
+ *             2^(ea[m,b] - 127) * 2^(ew[n,b] - 127) * sum_{k in b} a[m,k] * w[n,k]
+ * a: E4M3 [M, K] and a_e8m0 [M, K/32] (as from mxfp8_quantize); w: MXFP4
+ * codes [N, K/2] (element 2j in the low nibble of byte j) and w_e8m0
+ * [N, K/32] (as from mxfp4_quantize); C: [M, N] row-major, fp32 or bf16.
+ * Runs on the scaled FP8 x FP4 MFMA with no decode (its internal sum is
+ * not exact fp32: about 6e-5 relative per 64-element step).  K % 128 == 0
+ * on this build (else NVFP4_ERR_UNSUPPORTED); a and w 16-byte aligned,
+ * the scale arrays 4-byte aligned.
+ */
+nvfp4_status mx_gemm_w4a8(const uint8_t* a_fp8, const uint8_t* a_e8m0, int64_t M, int64_t K,
+                          const uint8_t* w_packed, const uint8_t* w_e8m0, int64_t N, void* C, nvfp4_dtype dtype,
+                          void* stream);
+
+/*
  * W4A16 GEMM (page "Qwen3.8-Flash-Next-FP4-Local", section 3.2: routed
  * experts of the MTP head keep their activations in BF16 and only the
  * weights in NVFP4):

@@ -22,7 +22,7 @@ __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
-    "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16",
+    "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
     "nvfp4_recipe", "status_string",
 ]
@@ -155,6 +155,35 @@ def mxfp4_quantize(x: torch.Tensor):
     _check(_lib.load().mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(packed), _ptr(e8),
                                       _stream(x.device)), "mxfp4_quantize")
     return packed, e8
+
+
+def mxfp8_quantize(x: torch.Tensor):
+    """bf16 [rows, cols] -> (E4M3 uint8 [rows, cols], e8m0 uint8 [rows, cols/32])."""
+    _need_cuda(x)
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    e8 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check(_lib.load().mxfp8_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(e8), _stream(x.device)),
+           "mxfp8_quantize")
+    return q, e8
+
+
+def mx_gemm_w4a8(a: torch.Tensor, a_e8m0: torch.Tensor, w_packed: torch.Tensor, w_e8m0: torch.Tensor,
+                 dtype=torch.float32, out: torch.Tensor | None = None):
+    """C[M, N] = a W^T with MXFP8 activations (E4M3 [M, K], e8m0 [M, K/32])
+    and MXFP4 weights (codes [N, K/2], e8m0 [N, K/32])."""
+    _need_cuda(a, a_e8m0, w_packed, w_e8m0)
+    for t in (a, a_e8m0, w_packed, w_e8m0):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("MX operands are contiguous uint8 tensors")
+    M, K = a.shape
+    N = w_packed.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=dtype, device=a.device)
+    code = _lib.BF16 if out.dtype == torch.bfloat16 else _lib.F32
+    _check(_lib.load().mx_gemm_w4a8(_ptr(a), _ptr(a_e8m0), M, K, _ptr(w_packed), _ptr(w_e8m0), N, _ptr(out),
+                                    code, _stream(a.device)), "mx_gemm_w4a8")
+    return out
 
 
 def mxfp4_to_nvfp4(packed: torch.Tensor, e8m0: torch.Tensor, rows: int, cols: int, batch: int = 1,

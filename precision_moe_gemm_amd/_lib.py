@@ -52,6 +52,8 @@ SIGNATURES = {
     "nvfp4_gemm": (ST, [TP, TP, P, ctypes.c_int, P, SZ, P]),
     "nvfp4_moe_grouped_gemm": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, P, SZ, P]),
     "nvfp4_gemm_w4a16": (ST, [P, I64, I64, I64, TP, P, ctypes.c_int, P, SZ, P]),
+    "mxfp8_quantize": (ST, [P, I64, I64, I64, P, P, P]),
+    "mx_gemm_w4a8": (ST, [P, P, I64, I64, P, P, I64, P, ctypes.c_int, P]),
     "nvfp4_moe_w4a16": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, SZ, P]),
     "nvfp4_moe_route": (ST, [P, I64, I32, I32, P, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up": (ST, [TP, P, P, I64, I32, I32, TP, P, P, P, SZ, P]),

@@ -10,6 +10,7 @@
 #include "gemm.h"
 #include "moe.h"
 #include "mx.h"
+#include "mx8.h"
 #include "quant.h"
 
 using namespace nvfp4;
@@ -713,6 +714,61 @@ nvfp4_status nvfp4_gemm_w4a16(const void* a, int64_t M, int64_t K, int64_t lda, 
         p.partial = (float*)ws;
     }
     return dispatch_dense(p, S(stream));
+}
+
+nvfp4_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* fp8, uint8_t* e8m0,
+                            void* stream)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || ld < cols || ld % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    const int64_t nblk = rows * (cols / 32);
+    if (nblk == 0)
+        return NVFP4_OK;
+    if (!x || !fp8 || !e8m0 || !aligned(x, 16) || !aligned(fp8, 16))
+        return NVFP4_ERR_INVALID_ARG;
+    mxfp8_encode_kernel<<<stream_grid(nblk, 8192), kMx8Threads, 0, S(stream)>>>(
+        (const u32x4*)x, rows, cols / 32, ld / 8, (u32x4*)fp8, e8m0);
+    return launch_status();
+}
+
+nvfp4_status mx_gemm_w4a8(const uint8_t* a, const uint8_t* a_e8m0, int64_t M, int64_t K, const uint8_t* w,
+                          const uint8_t* w_e8m0, int64_t N, void* C, nvfp4_dtype dtype, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return NVFP4_ERR_SHAPE;
+    if (dtype != NVFP4_F32 && dtype != NVFP4_BF16)
+        return NVFP4_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return NVFP4_OK;
+    if (K == 0 || K % kMxGrpK != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (!a || !a_e8m0 || !w || !w_e8m0 || !C || !aligned(a, 16) || !aligned(w, 16) || !aligned(a_e8m0, 4) ||
+        !aligned(w_e8m0, 4))
+        return NVFP4_ERR_INVALID_ARG;
+    MxArgs p{};
+    p.a = a;
+    p.a_sc = a_e8m0;
+    p.w = w;
+    p.w_sc = w_e8m0;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.out = C;
+    p.out_bf16 = dtype == NVFP4_BF16;
+    p.n_tiles = ceil_div(N, 256);
+    hipStream_t st = S(stream);
+    if (M >= 256) {
+        p.m_tiles = ceil_div(M, 256);
+        const int64_t blocks = ceil_div(p.m_tiles * p.n_tiles, 8) * 8;
+        if (blocks > 0x7FFFFFFF)
+            return NVFP4_ERR_SHAPE;
+        mx_w4a8_kernel<256, 256><<<(unsigned)blocks, 256, 0, st>>>(p);
+    } else {
+        p.m_tiles = ceil_div(M, 128);
+        const int64_t blocks = ceil_div(p.m_tiles * p.n_tiles, 8) * 8;
+        mx_w4a8_kernel<128, 256><<<(unsigned)blocks, 256, 0, st>>>(p);
+    }
+    return launch_status();
 }
 
 nvfp4_status nvfp4_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* perm,
