@@ -147,6 +147,16 @@ NVFP4_DEV uint32_t encode_half(u32x4 v, float r)
     return c;
 }
 
+// The value of lane (l ^ M) for lane l, within each group of 32 lanes
+// (ds_swizzle bit mode: the pattern is an immediate, no lane address).
+template <int M>
+NVFP4_DEV uint32_t swz_xor(uint32_t v)
+{
+    static_assert(M > 0 && M < 32, "xor within 32 lanes");
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));
+}
+NVFP4_DEV uint32_t umax_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
 // One NVFP4 block held by 16 consecutive lanes (lane 16 q + p holds
 // element p, as bf16 bits in the low half of hb), encoded as nvfp4_quantize
 // encodes it: the block max over the 16 lanes, block_scale, codes of x * r
@@ -156,23 +166,22 @@ NVFP4_DEV uint32_t encode_half(u32x4 v, float r)
 NVFP4_DEV void encode_block16(uint32_t hb, float G, float six_g, uint32_t* sc, uint32_t* codes)
 {
     uint32_t am = hb & 0x7FFFu;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)am, off, 64);
-        am = am > o ? am : o;
-    }
+    am = umax_u32(am, swz_xor<1>(am));
+    am = umax_u32(am, swz_xor<2>(am));
+    am = umax_u32(am, swz_xor<4>(am));
+    am = umax_u32(am, swz_xor<8>(am));
     const float r = block_scale(am, G, six_g, sc);
     const float x = __uint_as_float(hb << 16);
     float y = x * r;
     if (__builtin_isinf(r) && x == 0.0f)
         y = x;
-    const float yo = __shfl_xor(y, 1, 64);
+    const float yo = __uint_as_float(swz_xor<1>(__float_as_uint(y)));
     const int p = threadIdx.x & 15;
     // even lanes: elements p (low nibble) and p + 1 of byte p / 2
     const uint32_t b = FP4_PACK2(0u, y, yo, 0) & 0xFFu;
     uint32_t w = b << (8 * ((p >> 1) & 3));
-    w |= (uint32_t)__shfl_xor((int)w, 2, 64);
-    w |= (uint32_t)__shfl_xor((int)w, 4, 64);
+    w |= swz_xor<2>(w);
+    w |= swz_xor<4>(w);
     *codes = w;
 }
 

@@ -160,6 +160,16 @@ NVFP4_DEV int64_t xcd_item(int64_t items)
     return (j < per && it < items) ? it : -1;
 }
 
+// Load from a table that no kernel in flight writes (produced by an earlier
+// launch): through the constant address space, so that a uniform index
+// becomes a scalar load, counted apart from the vector loads in flight.
+template <class T>
+NVFP4_DEV T const_load(const T* ptr, int64_t i)
+{
+    typedef const __attribute__((address_space(4))) T* cptr;
+    return ((cptr)(uintptr_t)ptr)[i];
+}
+
 template <int V>
 struct IntC {
     static constexpr int value = V;
@@ -423,7 +433,7 @@ gemm_kernel(GemmArgs p)
     }
     u32x4 creg[2][RPT][2];
     const int64_t nstages = K / kBK;
-    auto load_stage = [&](int64_t st, int set) {
+    auto load_stage = [&](int st, int set) {
 #pragma unroll
         for (int i = 0; i < RPT; i++) {
             const u32x4* c = (const u32x4*)(csrc[i] + st * kStageCodeBytes);
@@ -1569,9 +1579,15 @@ namespace nvfp4 {
 // into an f16 LDS tile.  Inside a stage the K order is permuted the same way
 // for both operands: k-step kk = 4 q + d (q < 2, d < 4) gives lane group
 // kg = lane / 16 the stage elements [128 q + 32 kg + 8 d, +8).  When the
-// tiles alone cannot fill the chip, K is split over several workgroups
-// (dense mode only) and a second kernel adds their partial sums in a fixed
-// order.
+// tiles alone cannot fill the chip, K is split over several workgroups and a
+// second kernel adds their partial sums in a fixed order.
+//
+// The grid is persistent: as many workgroups as the chip holds at once, each
+// walking a list of (tile, K split) items with one register pipeline that
+// runs on from the last stages of one item into the first of the next, so
+// that the weight stream never waits for a new workgroup to start.  Item
+// set-up reads its tables (tile offsets, list positions) with scalar loads,
+// which are counted apart from the vector loads in flight.
 // ---------------------------------------------------------------------------
 constexpr int kSkBK = 256;               // K elements per stage
 constexpr int kSkRowF16 = kSkBK * 2;     // f16 A-tile bytes per row per stage
@@ -1599,85 +1615,131 @@ gemm_stream_kernel(GemmArgs p)
     const int lane = tid & 63, wave = tid >> 6;
     const int fr = lane & 15, kg = lane >> 4;
 
-    // ---- tile assignment: the A tile index varies fastest, so the tiles
-    // that share W rows run together on one XCD and share its L2 ----------
-    const int64_t m_act = MODE == kModeDense ? p.m_tiles : p.tile_off[p.experts];
-    const int64_t bid = xcd_item(m_act * p.n_tiles * p.ksplit);
-    if (bid < 0)
+    // ---- work items (A tile, K split, W tile), the A tile varying fastest.
+    // The grid is resident (a multiple of 8, at most what the chip holds) and
+    // each workgroup walks its items with one load pipeline that runs on from
+    // one item into the next.  XCD x (workgroups x, x + 8, ...) owns a
+    // contiguous eighth of the items, so the tiles that share W rows run
+    // together on one XCD and share its L2; within the XCD the items are
+    // dealt round-robin to its workgroups.  (Item counts stay below 2^31.)
+    const int m_act = MODE == kModeDense ? (int)p.m_tiles : const_load(p.tile_off, p.experts);
+    const int items = m_act * (int)p.n_tiles * p.ksplit;
+    const int per = (items + 7) >> 3;
+    const int x_begin = (int)(blockIdx.x & 7) * per;
+    const int x_end = x_begin + per < items ? x_begin + per : items;
+    if (x_begin >= x_end)
         return;
-    const int64_t mt = bid % m_act;
-    const int64_t rest = bid / m_act;
-    const int ks = (int)(rest % p.ksplit);
-    const int64_t nt = rest / p.ksplit;
-
-    int e = 0;
-    int64_t row_begin, row_end;
-    if (MODE == kModeDense) {
-        row_begin = mt * BM;
-        row_end = row_begin + BM < p.M ? row_begin + BM : p.M;
-    } else {
-        if (mt >= p.tile_off[p.experts])
-            return;
-        int lo = 0, hi = p.experts - 1;  // largest e with tile_off[e] <= mt
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.tile_off[mid] <= mt)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        e = lo;
-        row_begin = p.row_base[e] + (mt - p.tile_off[e]) * BM;
-        const int64_t eend = p.row_lim[e];
-        row_end = row_begin + BM < eend ? row_begin + BM : eend;
-    }
+    const int active = (int)(gridDim.x >> 3), slot = (int)(blockIdx.x >> 3);
+    if (x_begin + slot >= x_end)
+        return;
 
     const int64_t K = p.K;
     const int64_t kpb = K / 2, kpsb = K / 16;
+    const int nst_all = (int)(K / kSkBK);
     const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
-    const uint8_t* wp = p.w_packed + (int64_t)e * w_rows * kpb;
-    const uint8_t* wsc = p.w_scales + (int64_t)e * w_rows * kpsb;
 
-    // stages [st0, st0 + nstages) of this split
-    const int64_t nst_all = K / kSkBK;
-    const int64_t st0 = nst_all * ks / p.ksplit;
-    const int64_t nstages = nst_all * (ks + 1) / p.ksplit - st0;
-
-    // tile row r -> W row.  Wave w's fragment f is tile rows 32 w + 16 f +
-    // [0, 16); in gate_up mode fragment 0 holds gate rows and fragment 1 the
-    // matching up rows.
-    auto w_row_of = [&](int r) -> int64_t {
-        if (MODE == kModeGateUp) {
-            const int64_t c = nt * (BN / 2) + 16 * (r >> 5) + (r & 15);
-            return ((r >> 4) & 1) == 0 ? c : p.N + c;
+    // item -> expert, A-side rows [row_begin, row_end), W tile, K split and
+    // its stages [st0, st0 + nst)
+    struct Item {
+        int64_t row_begin, row_end, nt;
+        int e, ks, st0, nst;
+    };
+    auto item_of = [&](int it) {
+        Item t;
+        const uint32_t u = (uint32_t)it, ma = (uint32_t)m_act, sp = (uint32_t)p.ksplit;
+        const int mt = (int)(u % ma);
+        const uint32_t rest = u / ma;
+        t.ks = (int)(rest % sp);
+        t.nt = rest / sp;
+        t.e = 0;
+        if (MODE == kModeDense) {
+            t.row_begin = mt * BM;
+            t.row_end = t.row_begin + BM < p.M ? t.row_begin + BM : p.M;
+        } else {
+            int lo = 0, hi = p.experts - 1;  // largest e with tile_off[e] <= mt
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (const_load(p.tile_off, mid) <= mt)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            t.e = lo;
+            t.row_begin = const_load(p.row_base, lo) + (mt - const_load(p.tile_off, lo)) * BM;
+            const int64_t eend = const_load(p.row_lim, lo);
+            t.row_end = t.row_begin + BM < eend ? t.row_begin + BM : eend;
         }
-        const int64_t n = nt * BN + r;
-        return n < p.N ? n : p.N - 1;  // ragged last tile: reread a valid row, never stored
+        t.st0 = nst_all * t.ks / p.ksplit;
+        t.nst = nst_all * (t.ks + 1) / p.ksplit - t.st0;
+        return t;
+    };
+    // stages of item it (its K split's share of the nst_all stages)
+    auto item_nst = [&](int it) {
+        const int ks = (int)(((uint32_t)it / (uint32_t)m_act) % (uint32_t)p.ksplit);
+        return nst_all * (ks + 1) / p.ksplit - nst_all * ks / p.ksplit;
     };
 
     // ---- this thread's loads: W code pieces j (tile row 32 j + tid / 8,
     // piece tid % 8), then either a W scale row (threads < 128) or an A
     // piece (threads >= 128: A row (tid - 128) / 8, piece tid % 8) ---------
     const int pc = tid & 7;
-    const uint8_t* wsrc[4];
+    const bool loads_scales = tid < 128;
+    const int arow = (tid >> 3) & 15;
     int wdst[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int r = 32 * j + (tid >> 3);
-        wsrc[j] = wp + w_row_of(r) * kpb + st0 * (kSkBK / 2) + 16 * pc;
         wdst[j] = r * 128 + 16 * sk_wslot(r, pc);
     }
-    const bool loads_scales = tid < 128;
-    const int arow = (tid >> 3) & 15;
-    int64_t aq = row_begin + arow;
-    if (aq >= row_end)
-        aq = row_begin;  // padding rows repeat a valid row; never stored
-    const int64_t ar = MODE == kModeGateUp ? p.perm[aq] / p.topk : aq;
-    const uint8_t* xsrc = loads_scales ? wsc + w_row_of(tid) * kpsb + st0 * (kSkBK / 16)
-                                       : p.a_packed + ar * kpb + st0 * (kSkBK / 2) + 16 * pc;
-    const uint8_t* ysrc = p.a_scales + ar * kpsb + st0 * (kSkBK / 16) + 2 * pc;
-    // W4A16: A row ar as bf16, this thread's 32 elements (64 bytes) of a stage
-    const uint16_t* bsrc = A16 ? p.a_bf16 + ar * p.lda + st0 * kSkBK + 32 * pc : nullptr;
+    const uint8_t* wsrc[4];
+    const uint8_t* xsrc;
+    const uint8_t* ysrc;
+    const uint16_t* bsrc;  // W4A16: A row as bf16, this thread's 32 elements (64 bytes) of a stage
+    // point the loads at stage 0 of item t
+    auto setup_loads = [&](const Item& t) {
+        // the thread index passes through an empty asm statement, so that
+        // what is derived from it is formed here, once per item, rather than
+        // hoisted out of the stage loop into registers held throughout
+        int th = tid;
+        asm volatile("" : "+v"(th));
+        const int pc = th & 7, arow = (th >> 3) & 15;
+        const bool loads_scales = th < 128;
+        const uint8_t* wp = p.w_packed + (int64_t)t.e * w_rows * kpb;
+        const uint8_t* wsc = p.w_scales + (int64_t)t.e * w_rows * kpsb;
+        // tile row r -> W row.  Wave w's fragment f is tile rows 32 w + 16 f +
+        // [0, 16); in gate_up mode fragment 0 holds gate rows and fragment 1
+        // the matching up rows.
+        auto w_row_of = [&](int r) -> int64_t {
+            if (MODE == kModeGateUp) {
+                const int64_t c = t.nt * (BN / 2) + 16 * (r >> 5) + (r & 15);
+                return ((r >> 4) & 1) == 0 ? c : p.N + c;
+            }
+            const int64_t n = t.nt * BN + r;
+            return n < p.N ? n : p.N - 1;  // ragged last tile: reread a valid row, never stored
+        };
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            wsrc[j] = wp + w_row_of(32 * j + (th >> 3)) * kpb + t.st0 * (kSkBK / 2) + 16 * pc;
+        int64_t ar = t.row_begin + arow;
+        if (ar >= t.row_end)
+            ar = t.row_begin;  // padding rows repeat a valid row; never stored
+        if (MODE == kModeGateUp) {
+            // the tile's 16 list positions -> tokens: uniform (scalar) loads,
+            // each lane keeping the one of its own row
+            int32_t pv = 0;
+#pragma unroll
+            for (int i = 0; i < BM; i++) {
+                const int64_t q = t.row_begin + i < t.row_end ? t.row_begin + i : t.row_begin;
+                const int32_t v = const_load(p.perm, q);
+                pv = arow == i ? v : pv;
+            }
+            ar = pv / p.topk;
+        }
+        xsrc = loads_scales ? wsc + w_row_of(th) * kpsb + t.st0 * (kSkBK / 16)
+                            : p.a_packed + ar * kpb + t.st0 * (kSkBK / 2) + 16 * pc;
+        ysrc = p.a_scales + ar * kpsb + t.st0 * (kSkBK / 16) + 2 * pc;
+        bsrc = A16 ? p.a_bf16 + ar * p.lda + t.st0 * kSkBK + 32 * pc : nullptr;
+    };
 
     u32x4 wreg[3][4];
     u32x4 xreg[3];
@@ -1691,7 +1753,7 @@ gemm_stream_kernel(GemmArgs p)
         } else {
             const int64_t xo = loads_scales ? st * (kSkBK / 16) : st * (kSkBK / 2);
             xreg[set] = *(const u32x4*)(xsrc + xo);
-            if (!A16)
+            if (!A16 && !loads_scales)
                 yreg[set] = *(const uint16_t*)(ysrc + st * (kSkBK / 16));
         }
 #pragma unroll
@@ -1771,116 +1833,163 @@ gemm_stream_kernel(GemmArgs p)
         }
     };
 
-    // ---- pipeline: registers hold stages s+2 and s+3 in flight while stage
-    // s+1 goes to LDS and stage s is computed; one barrier per stage -------
-    const int64_t last = nstages - 1;
-    load_stage(0, 0);
-    load_stage(last < 1 ? last : 1, 1);
-    load_stage(last < 2 ? last : 2, 2);
-    store_stage(0, 0);
-    __syncthreads();
-    auto iter = [&](int64_t s, auto set_tag) {
-        constexpr int cur = decltype(set_tag)::value;  // register set of stage s (and s+3)
-        constexpr int nxt = (cur + 1) % 3;              // register set of stage s+1
-        store_stage(nxt, (int)((s + 1) & 1));
-        load_stage(s + 3 <= last ? s + 3 : last, cur);
-        compute((int)(s & 1));
-        __syncthreads();
-    };
-    int64_t s = 0;
-    for (; s + 3 <= nstages; s += 3) {
-        iter(s, IntC<0>{});
-        iter(s + 1, IntC<1>{});
-        iter(s + 2, IntC<2>{});
-    }
-    if (s < nstages)
-        iter(s, IntC<0>{});
-    if (s + 1 < nstages)
-        iter(s + 1, IntC<1>{});
-
-    // ---- epilogue: lane holds output rows 4 kg + i, column fr of each
-    // fragment ------------------------------------------------------------
-    const float gscale = (A16 ? 1.0f : *p.a_global) * p.w_global[e];
-    const int rows_left = (int)(row_end - row_begin);
-    if (MODE == kModeGateUp && p.ksplit > 1) {
-        // K split: scaled partial gate and up sums to plane ks, rows of 2N
-        // (gate columns, then up columns); swiglu_reduce_kernel finishes
-        const int64_t col = nt * (BN / 2) + 16 * wave + fr;
-        float* part = p.partial + (int64_t)ks * p.M * 2 * p.N;
+    // ---- epilogue of item t: lane holds output rows 4 kg + i, column fr of
+    // each fragment ---------------------------------------------------------
+    uint32_t hmax = 0;  // gate_up with bf16 h: max |h| bits seen by this lane
+    auto epilogue = [&](const Item& t) {
+        // (lane index made opaque as in setup_loads)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int fr = ln & 15, kg = ln >> 4;
+        const float gscale = (A16 ? 1.0f : const_load(p.a_global, 0)) * const_load(p.w_global, t.e);
+        const int rows_left = (int)(t.row_end - t.row_begin);
+        if (MODE == kModeGateUp && p.ksplit > 1) {
+            // K split: scaled partial gate and up sums to plane ks, rows of
+            // 2N (gate columns, then up columns); swiglu_reduce_kernel finishes
+            const int64_t col = t.nt * (BN / 2) + 16 * wave + fr;
+            float* part = p.partial + (int64_t)t.ks * p.M * 2 * p.N;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int m = 4 * kg + i;
-            if (m < rows_left) {
-                const int64_t o = (row_begin + m) * 2 * p.N + col;
-                part[o] = acc[0][i] * gscale;
-                part[o + p.N] = acc[1][i] * gscale;
+            for (int i = 0; i < 4; i++) {
+                const int m = 4 * kg + i;
+                if (m < rows_left) {
+                    const int64_t o = (t.row_begin + m) * 2 * p.N + col;
+                    part[o] = acc[0][i] * gscale;
+                    part[o + p.N] = acc[1][i] * gscale;
+                }
             }
-        }
-    } else if (MODE == kModeGateUp && p.hq_global) {
-        // h straight to NVFP4: the 16 lanes of a k-group hold the 16
-        // columns of one block of row 4 kg + i
-        const int64_t col = nt * (BN / 2) + 16 * wave + fr;
-        const float Gh = *p.hq_global, six = 6.0f * Gh;
+        } else if (MODE == kModeGateUp && p.hq_global) {
+            // h straight to NVFP4: the 16 lanes of a k-group hold the 16
+            // columns of one block of row 4 kg + i
+            const int64_t col = t.nt * (BN / 2) + 16 * wave + fr;
+            const float Gh = const_load(p.hq_global, 0), six = 6.0f * Gh;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int m = 4 * kg + i;
-            const float gg = acc[0][i] * gscale;
-            const float uu = acc[1][i] * gscale;
-            const uint32_t hb = f32_to_bf16(silu_f(gg) * uu);
-            uint32_t sc, codes;
-            encode_block16(hb, Gh, six, &sc, &codes);
-            if (m < rows_left) {
-                const int64_t row = row_begin + m;
-                if ((fr & 7) == 0)
-                    *(uint32_t*)(p.hq_packed + row * (p.N / 2) + (col >> 1)) = codes;
-                if (fr == 0)
-                    p.hq_scales[row * (p.N / 16) + (col >> 4)] = (uint8_t)sc;
-            }
-        }
-    } else if (MODE == kModeGateUp) {
-        const int64_t col = nt * (BN / 2) + 16 * wave + fr;
-        uint16_t* h = (uint16_t*)p.out + row_begin * p.N + col;
-        uint32_t hmax = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int m = 4 * kg + i;
-            if (m < rows_left) {
+            for (int i = 0; i < 4; i++) {
+                const int m = 4 * kg + i;
                 const float gg = acc[0][i] * gscale;
                 const float uu = acc[1][i] * gscale;
-                const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
-                h[(int64_t)m * p.N] = hb;
-                const uint32_t mag = hb & 0x7FFFu;
-                hmax = hmax > mag ? hmax : mag;
+                const uint32_t hb = f32_to_bf16(silu_f(gg) * uu);
+                uint32_t sc, codes;
+                encode_block16(hb, Gh, six, &sc, &codes);
+                if (m < rows_left) {
+                    const int64_t row = t.row_begin + m;
+                    if ((fr & 7) == 0)
+                        *(uint32_t*)(p.hq_packed + row * (p.N / 2) + (col >> 1)) = codes;
+                    if (fr == 0)
+                        p.hq_scales[row * (p.N / 16) + (col >> 4)] = (uint8_t)sc;
+                }
             }
-        }
-        hmax = wave_max_u32(hmax);
-        if (lane == 0 && hmax != 0)
-            atomicMax(p.h_amax, hmax << 16);
-    } else {
-        // K split: split ks writes its scaled partial sums to plane ks
-        const bool split = p.ksplit > 1;
-        const bool bf16_out = MODE == kModeDense && p.out_bf16;
-        float* part = split ? p.partial + (int64_t)ks * p.M * p.N : nullptr;
+        } else if (MODE == kModeGateUp) {
+            // h as bf16; its max magnitude is kept per lane over the items
+            // and goes to the atomic word once, after the last item
+            const int64_t col = t.nt * (BN / 2) + 16 * wave + fr;
+            uint16_t* h = (uint16_t*)p.out + t.row_begin * p.N + col;
 #pragma unroll
-        for (int f = 0; f < 2; f++) {
-            const int64_t col = nt * BN + 32 * wave + 16 * f + fr;
-            if (col < p.N) {
+            for (int i = 0; i < 4; i++) {
+                const int m = 4 * kg + i;
+                if (m < rows_left) {
+                    const float gg = acc[0][i] * gscale;
+                    const float uu = acc[1][i] * gscale;
+                    const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+                    h[(int64_t)m * p.N] = hb;
+                    const uint32_t mag = hb & 0x7FFFu;
+                    hmax = hmax > mag ? hmax : mag;
+                }
+            }
+        } else {
+            // K split: split ks writes its scaled partial sums to plane ks
+            const bool split = p.ksplit > 1;
+            const bool bf16_out = MODE == kModeDense && p.out_bf16;
+            float* part = split ? p.partial + (int64_t)t.ks * p.M * p.N : nullptr;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int m = 4 * kg + i;
-                    if (m < rows_left) {
-                        const int64_t o = (row_begin + m) * p.N + col;
-                        if (split)
-                            part[o] = acc[f][i] * gscale;
-                        else if (bf16_out)
-                            ((uint16_t*)p.out)[o] = f32_to_bf16(acc[f][i] * gscale);
-                        else
-                            ((float*)p.out)[o] = acc[f][i] * gscale;
+            for (int f = 0; f < 2; f++) {
+                const int64_t col = t.nt * BN + 32 * wave + 16 * f + fr;
+                if (col < p.N) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int m = 4 * kg + i;
+                        if (m < rows_left) {
+                            const int64_t o = (t.row_begin + m) * p.N + col;
+                            if (split)
+                                part[o] = acc[f][i] * gscale;
+                            else if (bf16_out)
+                                ((uint16_t*)p.out)[o] = f32_to_bf16(acc[f][i] * gscale);
+                            else
+                                ((float*)p.out)[o] = acc[f][i] * gscale;
+                        }
                     }
                 }
             }
         }
+    };
+
+    // ---- load cursor: runs three stages ahead of the compute cursor over
+    // the same item sequence; past the last item it rereads that item's last
+    // stage (never computed) ------------------------------------------------
+    int l_it = x_begin + slot, l_s = 0, l_nst;
+    {
+        const Item t = item_of(l_it);
+        setup_loads(t);
+        l_nst = t.nst;
     }
+    auto load_next = [&](int set) {
+        load_stage(l_s, set);
+        if (++l_s == l_nst) {
+            if (l_it + active < x_end) {
+                l_it += active;
+                const Item t = item_of(l_it);
+                setup_loads(t);
+                l_s = 0;
+                l_nst = t.nst;
+            } else {
+                l_s = l_nst - 1;
+            }
+        }
+    };
+
+    // ---- pipeline: registers hold stages g+2 and g+3 in flight while stage
+    // g+1 goes to LDS and stage g is computed; one barrier per stage -------
+    int c_it = x_begin + slot, c_s = 0, c_nst = item_nst(c_it);
+    int total = 0;  // stages this workgroup computes
+    for (int it = c_it; it < x_end; it += active)
+        total += item_nst(it);
+    load_next(0);
+    load_next(1);
+    load_next(2);
+    store_stage(0, 0);
+    __syncthreads();
+    int g = 0;  // stages computed so far; its parity picks the LDS buffer
+    auto iter = [&](auto set_tag) {
+        constexpr int cur = decltype(set_tag)::value;  // register set of stage g (and g+3)
+        constexpr int nxt = (cur + 1) % 3;              // register set of stage g+1
+        store_stage(nxt, (g + 1) & 1);
+        load_next(cur);
+        compute(g & 1);
+        __syncthreads();
+        g++;
+        if (++c_s == c_nst) {
+            epilogue(item_of(c_it));
+            acc[0] = (float4_t){};
+            acc[1] = (float4_t){};
+            c_it += active;
+            c_nst = item_nst(c_it);
+            c_s = 0;
+        }
+    };
+    while (g + 3 <= total) {
+        iter(IntC<0>{});
+        iter(IntC<1>{});
+        iter(IntC<2>{});
+    }
+    if (g < total)
+        iter(IntC<0>{});
+    if (g < total)
+        iter(IntC<1>{});
+    if (MODE == kModeGateUp && p.ksplit == 1 && !p.hq_global) {
+        hmax = wave_max_u32(hmax);
+        if (lane == 0 && hmax != 0)
+            atomicMax(p.h_amax, hmax << 16);
+    }
+    wait_vm<0>();  // the rereads past the last item
 }
 
 // K-split gate_up: h[r, c] = bf16(silu(g) * u) with g, u the sums in split

@@ -165,24 +165,54 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K)
     return s > 1 ? align256((size_t)s * M * N * sizeof(float)) : 0;
 }
 
+// Workgroups of a weight-streaming kernel that the current device holds at
+// once, rounded down to a multiple of 8 (one query per kernel and device).
+template <int MODE, bool P2, bool A16>
+int64_t stream_resident()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        dev = 0;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_stream_kernel<MODE, P2, A16>, kSkThreads, 0) !=
+                hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 8;
+        cached[dev] = std::max(8, per_cu * cus / 8 * 8);
+    }
+    return cached[dev];
+}
+
+template <int MODE, bool P2, bool A16>
+void launch_stream_kernel(const GemmArgs& p, int64_t items, hipStream_t st)
+{
+    // a resident grid (multiple of 8) that walks the items
+    const int64_t blocks = std::min(ceil_div(items, 8) * 8, stream_resident<MODE, P2, A16>());
+    gemm_stream_kernel<MODE, P2, A16><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+}
+
 template <int MODE>
 nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
 {
     p.m_tiles = m_tiles_ub;
-    int64_t blocks = m_tiles_ub * p.n_tiles * p.ksplit;
-    if (blocks == 0)
+    const int64_t items = m_tiles_ub * p.n_tiles * p.ksplit;
+    if (items == 0)
         return NVFP4_OK;
-    blocks = ceil_div(blocks, 8) * 8;
-    if (blocks > 0x7FFFFFFF)
+    // every K split holds at least one stage; item indices fit 31 bits
+    if (items > 0x7FFFFFFF || p.ksplit < 1 || p.ksplit > p.K / kSkBK)
         return NVFP4_ERR_SHAPE;
     if (p.a_bf16 && p.w_pow2)
-        gemm_stream_kernel<MODE, true, true><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+        launch_stream_kernel<MODE, true, true>(p, items, st);
     else if (p.a_bf16)
-        gemm_stream_kernel<MODE, false, true><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+        launch_stream_kernel<MODE, false, true>(p, items, st);
     else if (p.w_pow2)
-        gemm_stream_kernel<MODE, true, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+        launch_stream_kernel<MODE, true, false>(p, items, st);
     else
-        gemm_stream_kernel<MODE, false, false><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+        launch_stream_kernel<MODE, false, false>(p, items, st);
     nvfp4_status s = launch_status();
     if (s != NVFP4_OK || p.ksplit <= 1 || MODE == kModeDown)
         return s;  // grouped down: the combine adds the planes
