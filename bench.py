@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the breakdown of other rows")
     ap.add_argument("--profile-copy", action="store_true",
                     help="also launch a 1 GiB plain copy (counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the 384-expert decode rows (for profiling); prints their JSON")
     return ap.parse_args()
 
 
@@ -104,6 +106,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.decode_only:
+        print(json.dumps({"decode_rows": decode_rows(dev, stream, 10)}))
+        return
     cfg = synth.C4_PREFILL
     T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
 
@@ -275,6 +280,68 @@ def torch_index(a):
     return torch.from_numpy(a).to("cuda")
 
 
+def decode_rows(dev, st, it):
+    """The 384-expert decode batch (T=64): fused layer with dynamic and with
+    calibrated globals, the W4A16 layer, and the MXFP4 -> NVFP4 remap of its
+    w13 weights; each timed with HIP events."""
+    import numpy as np
+    import torch
+    import precision_moe_gemm_amd as nv
+    from precision_moe_gemm_amd import _lib, synth, workloads
+    res = {}
+
+    def gbs(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    c4 = synth.C4_DECODE
+    log("breakdown: 384-expert decode + remap")
+    W = workloads.build_moe_weights(c4, dev, keep_mx=True)
+    x = c4.x(dev)
+    ids, wt = workloads.routing(c4, dev)
+    ws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_MOE, c4.T, c4.k, c4.E, c4.H, c4.I), dtype=torch.uint8, device=dev)
+    out = torch.empty((c4.T, c4.H), dtype=torch.bfloat16, device=dev)
+    f = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, W.w13, W.w2, out=out, ws=ws)
+    f()
+    ms = time_loop(f, it, st)
+    touched = np.unique(ids.cpu().numpy())
+    wbytes = len(touched) * 3 * c4.H * c4.I * 0.5625
+    res["moe_384e_top8_decode_T64"] = {"ms": round(ms, 4), "experts_touched": int(len(touched)),
+                                       "touched_weight_GBps": gbs(wbytes, ms),
+                                       "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
+    # calibrated globals (from one dynamic staged pass): h encoded in the epilogue
+    xq4 = nv.nvfp4_quantize(x)
+    perm4, off4, _ = nv.nvfp4_moe_route(ids, c4.E)
+    _, hmax4 = nv.nvfp4_moe_gate_up(xq4, perm4, off4, c4.k, W.w13)
+    sg4 = torch.tensor([float(xq4.global_[0].item()),
+                        float(np.uint32(hmax4.item()).view(np.float32)) / 2688.0],
+                       dtype=torch.float32, device=dev)
+    f = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, W.w13, W.w2, static_in_globals=sg4, out=out, ws=ws)
+    f()
+    ms = time_loop(f, it, st)
+    res["moe_384e_top8_decode_T64_static_globals"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
+                                                      "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
+    # the same experts as W4A16 (bf16 activations, no activation quantization)
+    f = lambda: nv.nvfp4_moe_w4a16(x, ids, wt, W.w13, W.w2, out=out, ws=ws)
+    f()
+    ms = time_loop(f, it, st)
+    res["moe_384e_top8_w4a16_decode_T64"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
+                                             "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
+    p13, s13 = W.mx13
+    dst = nv.NVFP4Tensor.empty(2 * c4.I, c4.H, c4.E, dev)
+    rws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_REMAP, c4.E, 0, 0, 2 * c4.I, c4.H), dtype=torch.uint8, device=dev)
+    f = lambda: nv.mxfp4_to_nvfp4(p13, s13, 2 * c4.I, c4.H, c4.E, out=dst, ws=rws)
+    f()
+    ms = time_loop(f, 3, st)
+    nel = c4.E * 2 * c4.I * c4.H
+    res["remap_w13_384x4096x7168"] = {"ms": round(ms, 4), "GBps": gbs(nel * (0.5 + 1 / 32 + 0.5 + 1 / 16), ms),
+                                      "bytes_basis": "0.5+1/32 B/elem read, 0.5+1/16 B/elem written",
+                                      "frac_hbm": round(gbs(nel * 1.09375, ms) / PEAK_HBM_GBS, 4)}
+    del W, ws, out, dst, rws
+    torch.cuda.empty_cache()
+
+    return res
+
+
 def breakdown(args):
     """Other hot-path rows on their own configs (each timed with HIP events)."""
     import ctypes
@@ -368,52 +435,7 @@ def breakdown(args):
     del W, ws, out
     torch.cuda.empty_cache()
 
-    # 384-expert decode batch + remap throughput
-    c4 = synth.C4_DECODE
-    log("breakdown: 384-expert decode + remap")
-    W = workloads.build_moe_weights(c4, dev, keep_mx=True)
-    x = c4.x(dev)
-    ids, wt = workloads.routing(c4, dev)
-    ws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_MOE, c4.T, c4.k, c4.E, c4.H, c4.I), dtype=torch.uint8, device=dev)
-    out = torch.empty((c4.T, c4.H), dtype=torch.bfloat16, device=dev)
-    f = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, W.w13, W.w2, out=out, ws=ws)
-    f()
-    ms = time_loop(f, it, st)
-    touched = np.unique(ids.cpu().numpy())
-    wbytes = len(touched) * 3 * c4.H * c4.I * 0.5625
-    res["moe_384e_top8_decode_T64"] = {"ms": round(ms, 4), "experts_touched": int(len(touched)),
-                                       "touched_weight_GBps": gbs(wbytes, ms),
-                                       "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
-    # calibrated globals (from one dynamic staged pass): h encoded in the epilogue
-    xq4 = nv.nvfp4_quantize(x)
-    perm4, off4, _ = nv.nvfp4_moe_route(ids, c4.E)
-    _, hmax4 = nv.nvfp4_moe_gate_up(xq4, perm4, off4, c4.k, W.w13)
-    sg4 = torch.tensor([float(xq4.global_[0].item()),
-                        float(np.uint32(hmax4.item()).view(np.float32)) / 2688.0],
-                       dtype=torch.float32, device=dev)
-    f = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, W.w13, W.w2, static_in_globals=sg4, out=out, ws=ws)
-    f()
-    ms = time_loop(f, it, st)
-    res["moe_384e_top8_decode_T64_static_globals"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
-                                                      "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
-    # the same experts as W4A16 (bf16 activations, no activation quantization)
-    f = lambda: nv.nvfp4_moe_w4a16(x, ids, wt, W.w13, W.w2, out=out, ws=ws)
-    f()
-    ms = time_loop(f, it, st)
-    res["moe_384e_top8_w4a16_decode_T64"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
-                                             "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
-    p13, s13 = W.mx13
-    dst = nv.NVFP4Tensor.empty(2 * c4.I, c4.H, c4.E, dev)
-    rws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_REMAP, c4.E, 0, 0, 2 * c4.I, c4.H), dtype=torch.uint8, device=dev)
-    f = lambda: nv.mxfp4_to_nvfp4(p13, s13, 2 * c4.I, c4.H, c4.E, out=dst, ws=rws)
-    f()
-    ms = time_loop(f, 3, st)
-    nel = c4.E * 2 * c4.I * c4.H
-    res["remap_w13_384x4096x7168"] = {"ms": round(ms, 4), "GBps": gbs(nel * (0.5 + 1 / 32 + 0.5 + 1 / 16), ms),
-                                      "bytes_basis": "0.5+1/32 B/elem read, 0.5+1/16 B/elem written",
-                                      "frac_hbm": round(gbs(nel * 1.09375, ms) / PEAK_HBM_GBS, 4)}
-    del W, ws, out, dst, rws
-    torch.cuda.empty_cache()
+    res.update(decode_rows(dev, st, it))
 
     # KV cache 262144 x 4 x 256
     c5 = synth.C5
