@@ -75,6 +75,26 @@ def test_weight_streaming_shapes(orc, M, N, K):
     assert rel_err(gotb, R) <= GEMM_TOL + BF16_HALF_ULP
 
 
+@pytest.mark.parametrize("M,N,K", [(20, 128 * 500 + 64, 256), (32, 128 * 400 + 1, 512)])
+def test_weight_streaming_many_items(orc, M, N, K):
+    """More (A tile, W tile) items than the chip holds workgroups, so every
+    workgroup walks several items and its load pipeline crosses item
+    boundaries (one- and two-stage items, a ragged A tile and a ragged last
+    W tile); every output element is checked."""
+    x = synth.normal_bf16((M, K), 1.0, (312, M, K))
+    w = synth.normal_bf16((N, K), 0.02, (313, N, K))
+    step(f"gemm weight streaming, many items M={M} N={N} K={K}")
+    A, W = _q(x), _q(w)
+    C = nv.nvfp4_gemm(A, W)
+    Cb = nv.nvfp4_gemm(A, W, torch.bfloat16)
+    torch.cuda.synchronize()
+    R = orc.gemm(to_oracle(A), to_oracle(W))
+    err = rel_err(C.cpu().numpy(), R)
+    print(f"streaming many items M={M} N={N} K={K} rel err {err:.3e}")
+    assert err <= GEMM_TOL
+    assert rel_err(Cb.float().cpu().numpy(), R) <= GEMM_TOL + BF16_HALF_ULP
+
+
 def test_split_k_matches_unsplit_and_is_reproducible():
     M, N, K = 3, 1024, 8192
     A = _q(synth.normal_bf16((M, K), 1.0, (320, 0)))

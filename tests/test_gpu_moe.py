@@ -165,6 +165,15 @@ def test_small_moe_mx_experts_every_row(orc):
     _check_moe(orc, cfg)
 
 
+def test_moe_many_items_per_workgroup(orc):
+    """A decode-sized batch (every tile a 16-row streaming tile) whose gate_up
+    projection has more (tile, column tile) items than resident workgroups,
+    each one stage long (H = 256): the streaming pipeline crosses an item
+    boundary at every stage; every row checked."""
+    cfg = synth.MoE(seed=38, E=64, k=8, H=256, I=2048, T=64)
+    _check_moe(orc, cfg)
+
+
 def test_moe_512_experts_top10_sampled(orc):
     """512 experts, top-10, T=4096, H=4096, I=1024 at full size."""
     _check_moe(orc, synth.C3, sample_rows=24, sample_tokens=6)
