@@ -1602,11 +1602,14 @@ NVFP4_DEV int sk_wslot(int r, int c) { return c ^ ((r >> 1) & 7); }
 // 16-byte slot of f16 chunk c (of 32) in A tile row r
 NVFP4_DEV int sk_aslot(int r, int c) { return c ^ (r & 15); }
 
-template <int MODE, bool P2, bool A16>
+template <int MODE, bool P2, bool A16, int SBM>
 __global__ void __launch_bounds__(kSkThreads)
 gemm_stream_kernel(GemmArgs p)
 {
-    constexpr int BM = kSkBM, BN = kSkBN;
+    static_assert(SBM == 16 || SBM == 32, "16- or 32-row A tiles");
+    constexpr int BM = SBM, BN = kSkBN;
+    constexpr int NA = BM / 16;           // A fragments (MFMA 16 x 16 x 32 rows) per tile
+    constexpr bool kAllA = BM == 32;      // every thread loads a piece of the A tile
     __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][BN * 128];        // codes, 2 x 16 KiB
     __shared__ __attribute__((aligned(16))) uint8_t lds_ws[2][BN * 16];        // scales, 2 x 2 KiB
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kSkRowF16];  // f16 A, 2 x 8 KiB
@@ -1680,11 +1683,13 @@ gemm_stream_kernel(GemmArgs p)
     };
 
     // ---- this thread's loads: W code pieces j (tile row 32 j + tid / 8,
-    // piece tid % 8), then either a W scale row (threads < 128) or an A
-    // piece (threads >= 128: A row (tid - 128) / 8, piece tid % 8) ---------
+    // piece tid % 8), a W scale row (threads < 128) and an A piece (A row
+    // tid / 8 % BM, piece tid % 8): with 16-row tiles the threads >= 128
+    // load the A tile, with 32-row tiles every thread does --------------
     const int pc = tid & 7;
     const bool loads_scales = tid < 128;
-    const int arow = (tid >> 3) & 15;
+    const bool loads_a = kAllA || tid >= 128;
+    const int arow = (tid >> 3) & (BM - 1);
     int wdst[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -1692,7 +1697,8 @@ gemm_stream_kernel(GemmArgs p)
         wdst[j] = r * 128 + 16 * sk_wslot(r, pc);
     }
     const uint8_t* wsrc[4];
-    const uint8_t* xsrc;
+    const uint8_t* xsrc;    // 16-row tiles: W scale row or A piece; 32-row tiles: A piece
+    const uint8_t* ssrc;    // 32-row tiles: W scale row
     const uint8_t* ysrc;
     const uint16_t* bsrc;  // W4A16: A row as bf16, this thread's 32 elements (64 bytes) of a stage
     // point the loads at stage 0 of item t
@@ -1702,7 +1708,7 @@ gemm_stream_kernel(GemmArgs p)
         // hoisted out of the stage loop into registers held throughout
         int th = tid;
         asm volatile("" : "+v"(th));
-        const int pc = th & 7, arow = (th >> 3) & 15;
+        const int pc = th & 7, arow = (th >> 3) & (BM - 1);
         const bool loads_scales = th < 128;
         const uint8_t* wp = p.w_packed + (int64_t)t.e * w_rows * kpb;
         const uint8_t* wsc = p.w_scales + (int64_t)t.e * w_rows * kpsb;
@@ -1735,18 +1741,32 @@ gemm_stream_kernel(GemmArgs p)
             }
             ar = pv / p.topk;
         }
-        xsrc = loads_scales ? wsc + w_row_of(th) * kpsb + t.st0 * (kSkBK / 16)
-                            : p.a_packed + ar * kpb + t.st0 * (kSkBK / 2) + 16 * pc;
+        const uint8_t* wsrow = wsc + w_row_of(th & 127) * kpsb + t.st0 * (kSkBK / 16);
+        const uint8_t* apiece = p.a_packed + ar * kpb + t.st0 * (kSkBK / 2) + 16 * pc;
+        xsrc = (!kAllA && loads_scales) ? wsrow : apiece;
+        ssrc = wsrow;
         ysrc = p.a_scales + ar * kpsb + t.st0 * (kSkBK / 16) + 2 * pc;
         bsrc = A16 ? p.a_bf16 + ar * p.lda + t.st0 * kSkBK + 32 * pc : nullptr;
     };
 
     u32x4 wreg[3][4];
     u32x4 xreg[3];
+    u32x4 sreg[3];  // 32-row tiles: W scales (threads < 128)
     uint32_t yreg[3];
     u32x4 breg[3][4];
     auto load_stage = [&](int64_t st, int set) {
-        if (A16 && !loads_scales) {
+        if (kAllA) {
+            if (loads_scales)
+                sreg[set] = *(const u32x4*)(ssrc + st * (kSkBK / 16));
+            if (A16) {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    breg[set][i] = *(const u32x4*)(bsrc + st * kSkBK + 8 * i);
+            } else {
+                xreg[set] = *(const u32x4*)(xsrc + st * (kSkBK / 2));
+                yreg[set] = *(const uint16_t*)(ysrc + st * (kSkBK / 16));
+            }
+        } else if (A16 && !loads_scales) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 breg[set][i] = *(const u32x4*)(bsrc + st * kSkBK + 8 * i);
@@ -1765,14 +1785,14 @@ gemm_stream_kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < 4; j++)
             *(u32x4*)(&lds_w[b][wdst[j]]) = wreg[set][j];
-        if (loads_scales) {
-            *(u32x4*)(&lds_ws[b][16 * tid]) = xreg[set];
-        } else if (A16) {
+        if (loads_scales)
+            *(u32x4*)(&lds_ws[b][16 * tid]) = kAllA ? sreg[set] : xreg[set];
+        if (loads_a && A16) {
             uint8_t* rowp = &lds_a[b][arow * kSkRowF16];
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 *(u32x4*)(rowp + 16 * sk_aslot(arow, 4 * pc + i)) = breg[set][i];
-        } else {
+        } else if (loads_a) {
             const half2_t s2 = scales2<0>(yreg[set]);
             uint8_t* rowp = &lds_a[b][arow * kSkRowF16];
             const u32x4 cv = xreg[set];
@@ -1784,7 +1804,12 @@ gemm_stream_kernel(GemmArgs p)
     };
 
     typedef float float4_t __attribute__((ext_vector_type(4)));
-    float4_t acc[2] = {(float4_t){}, (float4_t){}};
+    float4_t acc[2][NA];  // [W fragment][A fragment]
+#pragma unroll
+    for (int f = 0; f < 2; f++)
+#pragma unroll
+        for (int a = 0; a < NA; a++)
+            acc[f][a] = (float4_t){};
 
     auto compute = [&](int b) {
         const uint8_t* ta = lds_a[b] + fr * kSkRowF16;
@@ -1808,7 +1833,10 @@ gemm_stream_kernel(GemmArgs p)
             }
 #pragma unroll
             for (int d = 0; d < 4; d++) {
-                const u32x4 fa = *(const u32x4*)(ta + 16 * sk_aslot(fr, 16 * q + 4 * kg + d));
+                u32x4 fa[NA];
+#pragma unroll
+                for (int a = 0; a < NA; a++)
+                    fa[a] = *(const u32x4*)(ta + 16 * a * kSkRowF16 + 16 * sk_aslot(16 * a + fr, 16 * q + 4 * kg + d));
 #pragma unroll
                 for (int f = 0; f < 2; f++) {
                     const u32x4 pv = piece[f];
@@ -1818,23 +1846,25 @@ gemm_stream_kernel(GemmArgs p)
                         // the fp8 byte pair converted exactly)
                         const float sc = P2 ? sf[f][d >> 1] : (float)(d < 2 ? s2[f].x : s2[f].y);
                         const u32x4 dv = P2 ? decode_chunk_bf16_p2(codes, sc) : decode_chunk_bf16(codes, sc);
-                        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa),
-                                                                         __builtin_bit_cast(bf16x8_t, dv), acc[f],
-                                                                         0, 0, 0);
+#pragma unroll
+                        for (int a = 0; a < NA; a++)
+                            acc[f][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, fa[a]), __builtin_bit_cast(bf16x8_t, dv), acc[f][a], 0, 0, 0);
                     } else {
                         const u32x4 dv = P2 ? decode_chunk_p2(codes, sf[f][d >> 1])
                                             : decode_chunk(codes, d < 2 ? s2[f].x : s2[f].y);
-                        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, fa),
-                                                                        __builtin_bit_cast(half8_t, dv), acc[f],
-                                                                        0, 0, 0);
+#pragma unroll
+                        for (int a = 0; a < NA; a++)
+                            acc[f][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(half8_t, fa[a]), __builtin_bit_cast(half8_t, dv), acc[f][a], 0, 0, 0);
                     }
                 }
             }
         }
     };
 
-    // ---- epilogue of item t: lane holds output rows 4 kg + i, column fr of
-    // each fragment ---------------------------------------------------------
+    // ---- epilogue of item t: lane holds output rows 16 a + 4 kg + i (A
+    // fragment a), column fr of each W fragment -------------------------------
     uint32_t hmax = 0;  // gate_up with bf16 h: max |h| bits seen by this lane
     auto epilogue = [&](const Item& t) {
         // (lane index made opaque as in setup_loads)
@@ -1849,52 +1879,58 @@ gemm_stream_kernel(GemmArgs p)
             const int64_t col = t.nt * (BN / 2) + 16 * wave + fr;
             float* part = p.partial + (int64_t)t.ks * p.M * 2 * p.N;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int m = 4 * kg + i;
-                if (m < rows_left) {
-                    const int64_t o = (t.row_begin + m) * 2 * p.N + col;
-                    part[o] = acc[0][i] * gscale;
-                    part[o + p.N] = acc[1][i] * gscale;
+            for (int a = 0; a < NA; a++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = 16 * a + 4 * kg + i;
+                    if (m < rows_left) {
+                        const int64_t o = (t.row_begin + m) * 2 * p.N + col;
+                        part[o] = acc[0][a][i] * gscale;
+                        part[o + p.N] = acc[1][a][i] * gscale;
+                    }
                 }
-            }
         } else if (MODE == kModeGateUp && p.hq_global) {
             // h straight to NVFP4: the 16 lanes of a k-group hold the 16
             // columns of one block of row 4 kg + i
             const int64_t col = t.nt * (BN / 2) + 16 * wave + fr;
             const float Gh = const_load(p.hq_global, 0), six = 6.0f * Gh;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int m = 4 * kg + i;
-                const float gg = acc[0][i] * gscale;
-                const float uu = acc[1][i] * gscale;
-                const uint32_t hb = f32_to_bf16(silu_f(gg) * uu);
-                uint32_t sc, codes;
-                encode_block16(hb, Gh, six, &sc, &codes);
-                if (m < rows_left) {
-                    const int64_t row = t.row_begin + m;
-                    if ((fr & 7) == 0)
-                        *(uint32_t*)(p.hq_packed + row * (p.N / 2) + (col >> 1)) = codes;
-                    if (fr == 0)
-                        p.hq_scales[row * (p.N / 16) + (col >> 4)] = (uint8_t)sc;
+            for (int a = 0; a < NA; a++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = 16 * a + 4 * kg + i;
+                    const float gg = acc[0][a][i] * gscale;
+                    const float uu = acc[1][a][i] * gscale;
+                    const uint32_t hb = f32_to_bf16(silu_f(gg) * uu);
+                    uint32_t sc, codes;
+                    encode_block16(hb, Gh, six, &sc, &codes);
+                    if (m < rows_left) {
+                        const int64_t row = t.row_begin + m;
+                        if ((fr & 7) == 0)
+                            *(uint32_t*)(p.hq_packed + row * (p.N / 2) + (col >> 1)) = codes;
+                        if (fr == 0)
+                            p.hq_scales[row * (p.N / 16) + (col >> 4)] = (uint8_t)sc;
+                    }
                 }
-            }
         } else if (MODE == kModeGateUp) {
             // h as bf16; its max magnitude is kept per lane over the items
             // and goes to the atomic word once, after the last item
             const int64_t col = t.nt * (BN / 2) + 16 * wave + fr;
             uint16_t* h = (uint16_t*)p.out + t.row_begin * p.N + col;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int m = 4 * kg + i;
-                if (m < rows_left) {
-                    const float gg = acc[0][i] * gscale;
-                    const float uu = acc[1][i] * gscale;
-                    const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
-                    h[(int64_t)m * p.N] = hb;
-                    const uint32_t mag = hb & 0x7FFFu;
-                    hmax = hmax > mag ? hmax : mag;
+            for (int a = 0; a < NA; a++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = 16 * a + 4 * kg + i;
+                    if (m < rows_left) {
+                        const float gg = acc[0][a][i] * gscale;
+                        const float uu = acc[1][a][i] * gscale;
+                        const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
+                        h[(int64_t)m * p.N] = hb;
+                        const uint32_t mag = hb & 0x7FFFu;
+                        hmax = hmax > mag ? hmax : mag;
+                    }
                 }
-            }
         } else {
             // K split: split ks writes its scaled partial sums to plane ks
             const bool split = p.ksplit > 1;
@@ -1905,18 +1941,20 @@ gemm_stream_kernel(GemmArgs p)
                 const int64_t col = t.nt * BN + 32 * wave + 16 * f + fr;
                 if (col < p.N) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int m = 4 * kg + i;
-                        if (m < rows_left) {
-                            const int64_t o = (t.row_begin + m) * p.N + col;
-                            if (split)
-                                part[o] = acc[f][i] * gscale;
-                            else if (bf16_out)
-                                ((uint16_t*)p.out)[o] = f32_to_bf16(acc[f][i] * gscale);
-                            else
-                                ((float*)p.out)[o] = acc[f][i] * gscale;
+                    for (int a = 0; a < NA; a++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int m = 16 * a + 4 * kg + i;
+                            if (m < rows_left) {
+                                const int64_t o = (t.row_begin + m) * p.N + col;
+                                if (split)
+                                    part[o] = acc[f][a][i] * gscale;
+                                else if (bf16_out)
+                                    ((uint16_t*)p.out)[o] = f32_to_bf16(acc[f][a][i] * gscale);
+                                else
+                                    ((float*)p.out)[o] = acc[f][a][i] * gscale;
+                            }
                         }
-                    }
                 }
             }
         }
@@ -1968,8 +2006,11 @@ gemm_stream_kernel(GemmArgs p)
         g++;
         if (++c_s == c_nst) {
             epilogue(item_of(c_it));
-            acc[0] = (float4_t){};
-            acc[1] = (float4_t){};
+#pragma unroll
+            for (int f = 0; f < 2; f++)
+#pragma unroll
+                for (int a = 0; a < NA; a++)
+                    acc[f][a] = (float4_t){};
             c_it += active;
             c_nst = item_nst(c_it);
             c_s = 0;

@@ -141,19 +141,25 @@ nvfp4_status launch_tile(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
 }
 
 // The weight-streaming kernel serves A operands of at most 32 rows per
-// expert (on average; tiles of 16 rows) when K is a multiple of its
+// expert (on average; tiles of 16 or 32 rows) when K is a multiple of its
 // 256-element stage.
 bool use_stream_gemm(int64_t rows_avg, int64_t K) { return rows_avg <= 2 * kSkBM && K > 0 && K % kSkBK == 0; }
 
+// Rows of a dense weight-streaming tile: 32 when A has more than 16 rows
+// (each W tile is then read once for all of them), else 16.
+int stream_bm(int64_t rows) { return rows > kSkBM ? 2 * kSkBM : kSkBM; }
+// Workgroups the chip holds at once of the bm-row streaming kernel
+// (3 per CU with 16-row tiles, 2 with 32-row tiles, 256 CUs).
+int64_t stream_slots(int bm) { return bm == kSkBM ? 768 : 512; }
+
 // K split of the dense weight-streaming GEMM: at most one workgroup per
-// resident slot (3 per CU on 256 CUs), at least four stages per split,
-// partials <= 32 MiB.
+// resident slot, at least four stages per split, partials <= 32 MiB.
 int gemm_ksplit(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || !use_stream_gemm(M, K))
         return 1;
-    const int64_t base = ceil_div(M, kSkBM) * ceil_div(N, kSkBN);
-    int64_t s = 768 / base;
+    const int64_t base = ceil_div(M, stream_bm(M)) * ceil_div(N, kSkBN);
+    int64_t s = stream_slots(stream_bm(M)) / base;
     s = std::min<int64_t>(s, K / kSkBK / 4);
     s = std::min<int64_t>(s, ((int64_t)32 << 20) / (M * N * 4));
     return (int)std::max<int64_t>(1, s);
@@ -167,7 +173,7 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K)
 
 // Workgroups of a weight-streaming kernel that the current device holds at
 // once, rounded down to a multiple of 8 (one query per kernel and device).
-template <int MODE, bool P2, bool A16>
+template <int MODE, bool P2, bool A16, int BM>
 int64_t stream_resident()
 {
     static int cached[64];
@@ -176,7 +182,7 @@ int64_t stream_resident()
         dev = 0;
     if (cached[dev] == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_stream_kernel<MODE, P2, A16>, kSkThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_stream_kernel<MODE, P2, A16, BM>, kSkThreads, 0) !=
                 hipSuccess ||
             per_cu < 1)
             per_cu = 1;
@@ -187,16 +193,31 @@ int64_t stream_resident()
     return cached[dev];
 }
 
-template <int MODE, bool P2, bool A16>
+template <int MODE, bool P2, bool A16, int BM>
 void launch_stream_kernel(const GemmArgs& p, int64_t items, hipStream_t st)
 {
     // a resident grid (multiple of 8) that walks the items
-    const int64_t blocks = std::min(ceil_div(items, 8) * 8, stream_resident<MODE, P2, A16>());
-    gemm_stream_kernel<MODE, P2, A16><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
+    const int64_t blocks = std::min(ceil_div(items, 8) * 8, stream_resident<MODE, P2, A16, BM>());
+    gemm_stream_kernel<MODE, P2, A16, BM><<<(unsigned)blocks, kSkThreads, 0, st>>>(p);
 }
 
+template <int MODE, int BM>
+void launch_stream_variant(const GemmArgs& p, int64_t items, hipStream_t st)
+{
+    if (p.a_bf16 && p.w_pow2)
+        launch_stream_kernel<MODE, true, true, BM>(p, items, st);
+    else if (p.a_bf16)
+        launch_stream_kernel<MODE, false, true, BM>(p, items, st);
+    else if (p.w_pow2)
+        launch_stream_kernel<MODE, true, false, BM>(p, items, st);
+    else
+        launch_stream_kernel<MODE, false, false, BM>(p, items, st);
+}
+
+// Weight-streaming GEMM over m_tiles_ub (an upper bound when grouped) A tiles
+// of bm (16 or 32) rows.
 template <int MODE>
-nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
+nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, int bm, hipStream_t st)
 {
     p.m_tiles = m_tiles_ub;
     const int64_t items = m_tiles_ub * p.n_tiles * p.ksplit;
@@ -205,14 +226,12 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     // every K split holds at least one stage; item indices fit 31 bits
     if (items > 0x7FFFFFFF || p.ksplit < 1 || p.ksplit > p.K / kSkBK)
         return NVFP4_ERR_SHAPE;
-    if (p.a_bf16 && p.w_pow2)
-        launch_stream_kernel<MODE, true, true>(p, items, st);
-    else if (p.a_bf16)
-        launch_stream_kernel<MODE, false, true>(p, items, st);
-    else if (p.w_pow2)
-        launch_stream_kernel<MODE, true, false>(p, items, st);
+    if (bm == 2 * kSkBM)
+        launch_stream_variant<MODE, 2 * kSkBM>(p, items, st);
+    else if (bm == kSkBM)
+        launch_stream_variant<MODE, kSkBM>(p, items, st);
     else
-        launch_stream_kernel<MODE, false, false>(p, items, st);
+        return NVFP4_ERR_SHAPE;
     nvfp4_status s = launch_status();
     if (s != NVFP4_OK || p.ksplit <= 1 || MODE == kModeDown)
         return s;  // grouped down: the combine adds the planes
@@ -237,7 +256,8 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
     if (p.a_bf16 || use_stream_gemm(p.M, p.K)) {
         // (W4A16 runs the weight-streaming kernel at every M)
         p.n_tiles = ceil_div(p.N, kSkBN);
-        return launch_stream_gemm<kModeDense>(p, ceil_div(p.M, kSkBM), st);
+        const int bm = stream_bm(p.M);
+        return launch_stream_gemm<kModeDense>(p, ceil_div(p.M, bm), bm, st);
     }
     p.ksplit = 1;
     p.n_tiles = ceil_div(p.N, 256);
@@ -250,30 +270,46 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
     return launch_gemm<32, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 32), st);
 }
 
+// Rows of the small tiles of a grouped projection with reduction length K
+// over `rows` (token, slot) pairs and E experts: 32-row tiles of the
+// register-decode kernel when K is not a multiple of the streaming stage;
+// else streaming tiles of 32 rows when every row takes them and the experts
+// average at least 32 rows (a dense MLP run as one expert: each W tile is
+// then read once), and of 16 rows otherwise.  (Measured: 32-row streaming
+// tiles run slower for the remainders next to the 128- and 256-row tiles and
+// for skewed decode batches, where most experts hold a few rows.)
+int grouped_small_bm(int64_t K, int all_small, int64_t rows, int32_t experts)
+{
+    if (K % kSkBK != 0)
+        return 32;
+    return (all_small && rows >= 2 * kSkBM * (int64_t)experts) ? 2 * kSkBM : kSkBM;
+}
+
 // K split of the grouped down projection of a tiny batch (a dense MLP run as
 // a one-expert layer, or a handful of tokens over few experts): every tile is
-// a 16-row weight-streaming tile and split s writes its scaled partial sums
-// to plane s of y, which the combine adds in split order.
-// Upper bound of the 16-row tiles the np pairs of a small batch fill: np/16
+// a weight-streaming tile and split s writes its scaled partial sums to plane
+// s of y, which the combine adds in split order.
+// Upper bound of the bm-row tiles the np pairs of a small batch fill: np/bm
 // full tiles plus at most one partial tile per other non-empty expert.
-int64_t small_tiles_est(int64_t np, int32_t E) { return std::min<int64_t>(np, ceil_div(np, kSkBM) + E - 1); }
+int64_t small_tiles_est(int64_t np, int32_t E, int bm) { return std::min<int64_t>(np, ceil_div(np, bm) + E - 1); }
 
 int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 {
     const int64_t np = T * k;
     if (np <= 0 || np > 256 || I % kSkBK != 0)
         return 1;
-    const int64_t tiles = small_tiles_est(np, E) * ceil_div(H, kSkBN);
-    if (tiles >= 512)
+    const int bm = grouped_small_bm(I, 1, np, E);
+    const int64_t tiles = small_tiles_est(np, E, bm) * ceil_div(H, kSkBN);
+    if (tiles >= stream_slots(bm) * 2 / 3)
         return 1;
-    int64_t s = 768 / tiles;
+    int64_t s = stream_slots(bm) / tiles;
     s = std::min<int64_t>(s, I / kSkBK / 4);
     s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * H * 4));
     return (int)std::max<int64_t>(1, s);
 }
 
 // K split of the fused gate_up projection of a tiny batch (as the down
-// projection): when the 16-row tiles cannot fill the chip, split s writes
+// projection): when the streaming tiles cannot fill the chip, split s writes
 // scaled partial gate and up sums to plane s and swiglu_reduce_kernel adds
 // the planes in order before the SwiGLU.  One wave of workgroups at most
 // (3 per CU), at least four 256-element stages per split.
@@ -282,10 +318,11 @@ int moe_gate_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
     const int64_t np = T * k;
     if (np <= 0 || np > 256 || H % kSkBK != 0)
         return 1;
-    const int64_t tiles = small_tiles_est(np, E) * ceil_div(I, kSkBN / 2);
-    if (tiles >= 512)
+    const int bm = grouped_small_bm(H, 1, np, E);
+    const int64_t tiles = small_tiles_est(np, E, bm) * ceil_div(I, kSkBN / 2);
+    if (tiles >= stream_slots(bm) * 2 / 3)
         return 1;
-    int64_t s = 768 / tiles;
+    int64_t s = stream_slots(bm) / tiles;
     s = std::min<int64_t>(s, H / kSkBK / 4);
     s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * 2 * I * 4));
     return (int)std::max<int64_t>(1, s);
@@ -294,8 +331,6 @@ int moe_gate_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 // Grouped projections: plan the tiles of every class on the device, then
 // launch each class (largest tiles first).  With p.ksplit > 1 (down only)
 // every tile is a 16-row streaming tile.
-// Streaming tile rows of a grouped projection with reduction length K.
-int grouped_small_bm(int64_t K) { return K % kSkBK == 0 ? kSkBM : 32; }
 
 // All rows of a grouped projection take 16-row weight-streaming tiles when
 // the down projection is K-split, or when the batch has at most 64 tokens:
@@ -314,13 +349,13 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
                               int all_small, int32_t* plan, bool plan_ready, hipStream_t st)
 {
     const bool stream_ok = p.K % kSkBK == 0;
-    const int small_bm = grouped_small_bm(p.K);
     if (p.a_bf16 && !stream_ok)
         return NVFP4_ERR_UNSUPPORTED;
     if (p.ksplit < 1 || !stream_ok)
         p.ksplit = 1;
     if (p.ksplit > 1 || p.a_bf16)
         all_small = 1;  // the split planes cover every row; W4A16 streams every tile
+    const int small_bm = grouped_small_bm(p.K, all_small, total_rows, experts);
     nvfp4_status s = NVFP4_OK;
     if (!plan_ready) {
         moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
@@ -356,15 +391,15 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
             return s;
     }
     GemmArgs q = cls(3);
-    // class 3: every tile holds at least one row; at most 4 tiles per expert
-    // (64 rows) unless all rows take small tiles, then at most one partial
-    // tile per non-empty expert
+    // class 3: every tile holds at least one row; at most 64 rows per expert
+    // (4 tiles of 16 or 2 of 32) unless all rows take small tiles, then at
+    // most one partial tile per non-empty expert
     const int64_t m_small =
         all_small ? std::min<int64_t>(total_rows, total_rows / small_bm + std::min<int64_t>(experts, total_rows))
                   : std::min<int64_t>((int64_t)experts * 4, total_rows);
     if (stream_ok) {
         q.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? kSkBN / 2 : kSkBN);
-        return launch_stream_gemm<MODE>(q, m_small, st);
+        return launch_stream_gemm<MODE>(q, m_small, small_bm, st);
     }
     q.ksplit = 1;
     q.n_tiles = ceil_div(p.N, big_cols);
@@ -1010,8 +1045,9 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     const bool small = T * k <= kRouteSmall;
     if (small)
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
-                       grouped_small_bm(H), grouped_all_small(T, H, gsplit), at<int32_t>(ws, L.r.plan_dn),
-                       grouped_small_bm(I), grouped_all_small(T, I, ksplit));
+                       grouped_small_bm(H, grouped_all_small(T, H, gsplit), T * k, E), grouped_all_small(T, H, gsplit),
+                       at<int32_t>(ws, L.r.plan_dn), grouped_small_bm(I, grouped_all_small(T, I, ksplit), T * k, E),
+                       grouped_all_small(T, I, ksplit));
     else
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
     if (s != NVFP4_OK)
@@ -1084,7 +1120,8 @@ nvfp4_status nvfp4_moe_w4a16(const void* x, const int32_t* ids, const float* w, 
     const bool small = T * k <= kRouteSmall;
     if (small)
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
-                       kSkBM, 1, at<int32_t>(ws, L.r.plan_dn), kSkBM, 1);
+                       grouped_small_bm(H, 1, T * k, E), 1, at<int32_t>(ws, L.r.plan_dn),
+                       grouped_small_bm(I, 1, T * k, E), 1);
     else
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
     if (s != NVFP4_OK)
