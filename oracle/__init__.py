@@ -91,6 +91,8 @@ def _load():
             "orc_moe_w4a16_down": (ctypes.c_int, [P, P, i32, P, P, P, i64, i64, P, i64, P]),
             "orc_mxfp8_encode": (ctypes.c_int, [P, i64, i64, i64, P, P]),
             "orc_mx_gemm_w4a8_rows": (ctypes.c_int, [P, P, P, i64, P, P, P, i64, i64, P]),
+            "orc_mx_moe_gate_up": (ctypes.c_int, [P, P, P, P, i32, i32, P, P, i64, i64, P, i64, P]),
+            "orc_mx_moe_down": (ctypes.c_int, [P, P, P, i32, P, P, i64, i64, P, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -494,3 +496,53 @@ def audit_scales(t: NVFP4) -> dict:
     nonpos = int(np.count_nonzero((s == 0) | ((s & 0x80) != 0)))
     return dict(total=int(s.size), nonfinite=nan, nonpositive=nonpos,
                 at_max=int(np.count_nonzero(s == 0x7E)))
+
+
+# --------------------------------------------------------------------------
+# MX-native W4A8 routed experts (MXFP4 experts, MXFP8 activations)
+# --------------------------------------------------------------------------
+
+def mx_moe_gate_up(xq, xe, perm, offsets, k: int, w13p, w13e, rows) -> np.ndarray:
+    """h (bf16 bits) [len(rows), I] for list positions ``rows``: x MXFP8
+    (codes [T, H], e8m0 [T, H/32]), w13 MXFP4 (codes [E, 2I, H/2], e8m0
+    [E, 2I, H/32]) (see orc_mx_moe_gate_up)."""
+    xq, xe = np.ascontiguousarray(xq, np.uint8), np.ascontiguousarray(xe, np.uint8)
+    w13p, w13e = np.ascontiguousarray(w13p, np.uint8), np.ascontiguousarray(w13e, np.uint8)
+    E, twoI, H = w13p.shape[0], w13p.shape[1], w13p.shape[2] * 2
+    I = twoI // 2
+    rows = np.ascontiguousarray(rows, np.int64)
+    h = np.zeros((rows.size, I), np.uint16)
+    _check(_load().orc_mx_moe_gate_up(_p(xq), _p(xe), _p(np.ascontiguousarray(perm, np.int32)),
+                                      _p(np.ascontiguousarray(offsets, np.int32)), k, E, _p(w13p), _p(w13e),
+                                      H, I, _p(rows), rows.size, _p(h)), "mx_moe_gate_up")
+    return h
+
+
+def mx_moe_down(hq, he, offsets, w2p, w2e, rows) -> np.ndarray:
+    """y (float64) [len(rows), H] for list positions ``rows``: h MXFP8 in list
+    order (codes [T*k, I], e8m0 [T*k, I/32]), w2 MXFP4 (codes [E, H, I/2],
+    e8m0 [E, H, I/32]) (see orc_mx_moe_down)."""
+    hq, he = np.ascontiguousarray(hq, np.uint8), np.ascontiguousarray(he, np.uint8)
+    w2p, w2e = np.ascontiguousarray(w2p, np.uint8), np.ascontiguousarray(w2e, np.uint8)
+    E, H, I = w2p.shape[0], w2p.shape[1], w2p.shape[2] * 2
+    rows = np.ascontiguousarray(rows, np.int64)
+    y = np.zeros((rows.size, H), np.float64)
+    _check(_load().orc_mx_moe_down(_p(hq), _p(he), _p(np.ascontiguousarray(offsets, np.int32)), E, _p(w2p),
+                                   _p(w2e), H, I, _p(rows), rows.size, _p(y)), "mx_moe_down")
+    return y
+
+
+def mx_moe_forward(x: np.ndarray, ids: np.ndarray, w: np.ndarray, w13p, w13e, w2p, w2e):
+    """Whole MX W4A8 routed-expert forward on bf16 x [T, H]: route -> x to
+    MXFP8 -> gate_up + SwiGLU -> h to MXFP8 (list order) -> down -> combine.
+    Returns every intermediate (xq, xe, perm, offsets, inv, h, hq, he, y, out)."""
+    E = w13p.shape[0]
+    T, k = ids.shape
+    perm, offsets, inv = moe_route(ids, E)
+    xq, xe = mxfp8_encode(x)
+    rows = np.arange(T * k, dtype=np.int64)
+    h = mx_moe_gate_up(xq, xe, perm, offsets, k, w13p, w13e, rows)
+    hq, he = mxfp8_encode(h)
+    y = mx_moe_down(hq, he, offsets, w2p, w2e, rows)
+    out = moe_combine(y, inv, w)
+    return dict(xq=xq, xe=xe, perm=perm, offsets=offsets, inv=inv, h=h, hq=hq, he=he, y=y, out=out)

@@ -891,3 +891,88 @@ int orc_mx_gemm_w4a8_rows(const uint8_t* A, const uint8_t* Ae, const int64_t* a_
         }
     return ORC_OK;
 }
+
+/*
+ * MX-native W4A8 routed-expert projections (page "DeepSeek-V4.1-Flash-NVFP4",
+ * section 二: MXFP4 expert weights with FP8 activations), for listed pairs,
+ * in the same steps as orc_moe_gate_up / orc_moe_down with the MX row
+ * product of orc_mx_gemm_w4a8_rows in place of the NVFP4 one:
+ *   gate_up: for list position q (rows[i]), token t = perm[q] / k, expert e
+ *     (offsets[e] <= q < offsets[e+1]): g, u = the MX products of x row t
+ *     with W13[e] rows [0, I) and [I, 2I); h = bf16(silu(g) * u) (double
+ *     SwiGLU, nearest-even).  x: E4M3 [T, H] + UE8M0 [T, H/32]; W13: codes
+ *     [E, 2I, H/2] + UE8M0 [E, 2I, H/32].  h_out: [n_rows, I] bf16 bits.
+ *   down: y[i] = the MX products of hq row rows[i] (list order, E4M3
+ *     [T*k, I] + UE8M0 [T*k, I/32]) with W2[e] ([E, H, I/2] + [E, H, I/32]).
+ *     y_out: [n_rows, H] double.
+ */
+static int orc_expert_of(const int32_t* offsets, int32_t E, int64_t q)
+{
+    int32_t e = 0;
+    while (e < E && !(offsets[e] <= q && q < offsets[e + 1]))
+        e++;
+    return e;
+}
+
+int orc_mx_moe_gate_up(const uint8_t* xq, const uint8_t* xe, const int32_t* perm, const int32_t* offsets,
+                       int32_t k, int32_t E, const uint8_t* w13p, const uint8_t* w13e, int64_t H, int64_t I,
+                       const int64_t* rows, int64_t n_rows, uint16_t* h_out)
+{
+    int64_t i, n, *w_rows;
+    double* gu;
+    int rc = ORC_OK;
+    if (H % 32 != 0)
+        return ORC_SHAPE;
+    w_rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * I));
+    gu = (double*)malloc(sizeof(double) * (size_t)(2 * I));
+    if (!w_rows || !gu) {
+        free(w_rows);
+        free(gu);
+        return ORC_INVALID;
+    }
+    for (n = 0; n < 2 * I; n++)
+        w_rows[n] = n;
+    for (i = 0; i < n_rows && rc == ORC_OK; i++) {
+        const int64_t q = rows[i];
+        const int32_t e = orc_expert_of(offsets, E, q);
+        int64_t a_row;
+        if (e == E) {
+            rc = ORC_RANGE;
+            break;
+        }
+        a_row = perm[q] / k;
+        rc = orc_mx_gemm_w4a8_rows(xq, xe, &a_row, 1, w13p + (size_t)e * (size_t)(2 * I) * (size_t)(H / 2),
+                                   w13e + (size_t)e * (size_t)(2 * I) * (size_t)(H / 32), w_rows, 2 * I, H, gu);
+        for (n = 0; n < I; n++)
+            h_out[i * I + n] = orc_bf16_from_double(silu(gu[n]) * gu[I + n]);
+    }
+    free(w_rows);
+    free(gu);
+    return rc;
+}
+
+int orc_mx_moe_down(const uint8_t* hq, const uint8_t* he, const int32_t* offsets, int32_t E, const uint8_t* w2p,
+                    const uint8_t* w2e, int64_t H, int64_t I, const int64_t* rows, int64_t n_rows, double* y_out)
+{
+    int64_t i, n, *w_rows;
+    int rc = ORC_OK;
+    if (I % 32 != 0)
+        return ORC_SHAPE;
+    w_rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)H);
+    if (!w_rows)
+        return ORC_INVALID;
+    for (n = 0; n < H; n++)
+        w_rows[n] = n;
+    for (i = 0; i < n_rows && rc == ORC_OK; i++) {
+        const int64_t q = rows[i];
+        const int32_t e = orc_expert_of(offsets, E, q);
+        if (e == E) {
+            rc = ORC_RANGE;
+            break;
+        }
+        rc = orc_mx_gemm_w4a8_rows(hq, he, &q, 1, w2p + (size_t)e * (size_t)H * (size_t)(I / 2),
+                                   w2e + (size_t)e * (size_t)H * (size_t)(I / 32), w_rows, H, I, y_out + i * H);
+    }
+    free(w_rows);
+    return rc;
+}
