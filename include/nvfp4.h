@@ -97,7 +97,8 @@ enum {
     NVFP4_OP_REMAP = 1,    /* mxfp4_to_nvfp4 (T = batch)           */
     NVFP4_OP_GEMM = 2,     /* nvfp4_gemm                            */
     NVFP4_OP_MOE = 3,      /* nvfp4_moe_grouped_gemm                */
-    NVFP4_OP_MOE_ROUTE = 4 /* nvfp4_moe_route / the staged GEMMs    */
+    NVFP4_OP_MOE_ROUTE = 4, /* nvfp4_moe_route / the staged GEMMs   */
+    NVFP4_OP_MX_MOE = 5     /* mx_moe_w4a8                          */
 };
 
 /* Bytes of `ws` an operation needs.  Unused arguments may be 0:
@@ -228,6 +229,47 @@ nvfp4_status mxfp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, int6
 nvfp4_status mx_gemm_w4a8(const uint8_t* a_fp8, const uint8_t* a_e8m0, int64_t M, int64_t K,
                           const uint8_t* w_packed, const uint8_t* w_e8m0, int64_t N, void* C, nvfp4_dtype dtype,
                           void* stream);
+
+/*
+ * MX-native W4A8 routed-expert layer (page "DeepSeek-V4.1-Flash-NVFP4",
+ * section 二: MXFP4 expert weights with FP8 activations; the layer as the
+ * NVFP4 one, page "Qwen3.8-Flash-Next-NVFP4", section 核心):
+ *   1. route the T x k (token, slot) pairs by expert (as nvfp4_moe_route);
+ *   2. x (bf16 [T, H]) -> MXFP8 (as mxfp8_quantize);
+ *   3. per pair (t, j) with e = ids[t, j]: g || u = the MX GEMM of x row t
+ *      with w13[e] (gate rows 0..I-1, up rows I..2I-1), h = bf16(silu(g) u);
+ *   4. h -> MXFP8 (as mxfp8_quantize, rows in list order);
+ *   5. y = the MX GEMM of the h row with w2[e] (fp32);
+ *   6. out[t] = bf16(sum_j w[t, j] y[t, j]), j ascending, in fp32.
+ * w13: MXFP4 codes [E, 2I, H/2] and UE8M0 scales [E, 2I, H/32]; w2: codes
+ * [E, H, I/2] and scales [E, H, I/32] (as from mxfp4_quantize per expert).
+ * ids int32 [T, k] in [0, E) (others raise NVFP4_ERR_RANGE and the pair
+ * is dropped); w fp32 [T, k]; out bf16 [T, H] (16-byte aligned).
+ * H % 256 == 0 and I % 128 == 0 on this build (else NVFP4_ERR_UNSUPPORTED).
+ * ws: nvfp4_workspace_size(NVFP4_OP_MX_MOE, T, k, E, H, I) bytes, 256-byte
+ * aligned, caller-owned; too small gives NVFP4_ERR_WORKSPACE.
+ */
+/*
+ * The two projections of mx_moe_w4a8 on their own (steps 3 and 5 there), for
+ * staged use and parity tests, with perm / offsets as from nvfp4_moe_route:
+ *   mx_moe_gate_up: x MXFP8 [T, H] (E4M3 codes, UE8M0 [T, H/32]) -> h bf16
+ *     [T*k, I] in list order; max |h| as float bits goes to *h_amax by
+ *     atomic max (the caller zeroes it first).
+ *   mx_moe_down: h MXFP8 [T*k, I] in list order -> y fp32 [T*k, H].
+ * Shapes, alignment and errors as mx_moe_w4a8; ws: as nvfp4_moe_route.
+ */
+nvfp4_status mx_moe_gate_up(const uint8_t* x_fp8, const uint8_t* x_e8m0, const int32_t* perm,
+                            const int32_t* offsets, int64_t T, int32_t k, int32_t E, int64_t H, int64_t I,
+                            const uint8_t* w13_packed, const uint8_t* w13_e8m0, void* h_bf16, uint32_t* h_amax,
+                            void* ws, size_t ws_bytes, void* stream);
+nvfp4_status mx_moe_down(const uint8_t* h_fp8, const uint8_t* h_e8m0, const int32_t* offsets, int64_t T, int32_t k,
+                         int32_t E, int64_t H, int64_t I, const uint8_t* w2_packed, const uint8_t* w2_e8m0,
+                         float* y, void* ws, size_t ws_bytes, void* stream);
+
+nvfp4_status mx_moe_w4a8(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, int64_t T, int32_t k,
+                         int32_t E, int64_t H, int64_t I, const uint8_t* w13_packed, const uint8_t* w13_e8m0,
+                         const uint8_t* w2_packed, const uint8_t* w2_e8m0, void* out_bf16, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /*
  * W4A16 GEMM (page "Qwen3.8-Flash-Next-FP4-Local", section 3.2: routed

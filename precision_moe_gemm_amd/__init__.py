@@ -22,7 +22,7 @@ __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
-    "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8",
+    "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8", "mx_moe_w4a8", "mx_moe_gate_up", "mx_moe_down",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
     "nvfp4_recipe", "status_string",
 ]
@@ -184,6 +184,62 @@ def mx_gemm_w4a8(a: torch.Tensor, a_e8m0: torch.Tensor, w_packed: torch.Tensor, 
     _check(_lib.load().mx_gemm_w4a8(_ptr(a), _ptr(a_e8m0), M, K, _ptr(w_packed), _ptr(w_e8m0), N, _ptr(out),
                                     code, _stream(a.device)), "mx_gemm_w4a8")
     return out
+
+
+def mx_moe_w4a8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13: torch.Tensor,
+                w13_e8m0: torch.Tensor, w2: torch.Tensor, w2_e8m0: torch.Tensor, out: torch.Tensor | None = None,
+                ws: torch.Tensor | None = None):
+    """MX-native W4A8 routed-expert MoE forward: bf16 x [T, H] -> bf16 [T, H]
+    with MXFP4 experts (w13 codes [E, 2I, H/2], e8m0 [E, 2I, H/32]; w2 codes
+    [E, H, I/2], e8m0 [E, H, I/32]) and MXFP8 activations."""
+    _need_cuda(x, topk_ids, topk_w, w13, w13_e8m0, w2, w2_e8m0)
+    for t in (w13, w13_e8m0, w2, w2_e8m0):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("MX expert operands are contiguous uint8 tensors")
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E, I2 = w13.shape[0], w13.shape[1]
+    I = I2 // 2
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MX_MOE, T, k, E, H, I), x.device)
+    _check(_lib.load().mx_moe_w4a8(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, E, H, I, _ptr(w13), _ptr(w13_e8m0), _ptr(w2), _ptr(w2_e8m0),
+        _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)), "mx_moe_w4a8")
+    return out
+
+
+def mx_moe_gate_up(xq: torch.Tensor, xe: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                   w13: torch.Tensor, w13_e8m0: torch.Tensor, ws: torch.Tensor | None = None):
+    """MX gate_up + SwiGLU: MXFP8 x (codes [T, H], e8m0 [T, H/32]) -> (h bf16
+    [T*k, I] in list order, max |h| as float bits)."""
+    T, H = xq.shape
+    E, I = w13.shape[0], w13.shape[1] // 2
+    dev = xq.device
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    hmax = torch.zeros(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE_ROUTE, T, k, E), dev)
+    _check(_lib.load().mx_moe_gate_up(_ptr(xq), _ptr(xe), _ptr(perm), _ptr(offsets), T, k, E, H, I, _ptr(w13),
+                                      _ptr(w13_e8m0), _ptr(h), _ptr(hmax), _ptr(ws), ws.numel(), _stream(dev)),
+           "mx_moe_gate_up")
+    return h, hmax
+
+
+def mx_moe_down(hq: torch.Tensor, he: torch.Tensor, offsets: torch.Tensor, T: int, k: int, w2: torch.Tensor,
+                w2_e8m0: torch.Tensor, ws: torch.Tensor | None = None):
+    """MX down: MXFP8 h (codes [T*k, I], e8m0 [T*k, I/32], list order) -> y
+    fp32 [T*k, H]."""
+    E, H = w2.shape[0], w2.shape[1]
+    I = hq.shape[1]
+    dev = hq.device
+    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(nvfp4_workspace_size(_lib.OP_MOE_ROUTE, T, k, E), dev)
+    _check(_lib.load().mx_moe_down(_ptr(hq), _ptr(he), _ptr(offsets), T, k, E, H, I, _ptr(w2), _ptr(w2_e8m0),
+                                   _ptr(y), _ptr(ws), ws.numel(), _stream(dev)), "mx_moe_down")
+    return y
 
 
 def mxfp4_to_nvfp4(packed: torch.Tensor, e8m0: torch.Tensor, rows: int, cols: int, batch: int = 1,

@@ -17,7 +17,7 @@ _lib = None
 
 OK, INVALID_ARG, SHAPE, RANGE, WORKSPACE, DEVICE, UNSUPPORTED = range(7)
 F32, BF16 = 0, 1
-OP_QUANTIZE, OP_REMAP, OP_GEMM, OP_MOE, OP_MOE_ROUTE = range(5)
+OP_QUANTIZE, OP_REMAP, OP_GEMM, OP_MOE, OP_MOE_ROUTE, OP_MX_MOE = range(6)
 
 
 class NVFP4TensorC(ctypes.Structure):
@@ -54,6 +54,10 @@ SIGNATURES = {
     "nvfp4_gemm_w4a16": (ST, [P, I64, I64, I64, TP, P, ctypes.c_int, P, SZ, P]),
     "mxfp8_quantize": (ST, [P, I64, I64, I64, P, P, P]),
     "mx_gemm_w4a8": (ST, [P, P, I64, I64, P, P, I64, P, ctypes.c_int, P]),
+    "mx_moe_w4a8": (ST, [P, P, P, I64, ctypes.c_int32, ctypes.c_int32, I64, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    "mx_moe_gate_up": (ST, [P, P, P, P, I64, ctypes.c_int32, ctypes.c_int32, I64, I64, P, P, P, P, P, ctypes.c_size_t,
+                            P]),
+    "mx_moe_down": (ST, [P, P, P, I64, ctypes.c_int32, ctypes.c_int32, I64, I64, P, P, P, P, ctypes.c_size_t, P]),
     "nvfp4_moe_w4a16": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, SZ, P]),
     "nvfp4_moe_route": (ST, [P, I64, I32, I32, P, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up": (ST, [TP, P, P, I64, I32, I32, TP, P, P, P, SZ, P]),

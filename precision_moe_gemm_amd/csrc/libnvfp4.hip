@@ -495,6 +495,133 @@ nvfp4_status route_impl(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
 
 // ======================================================================== ABI
 
+// ---------------------------------------------------------------- MX MoE
+// Workspace of mx_moe_w4a8: routing, one tile plan (both projections share
+// the expert offsets), MXFP8 x, h (bf16), MXFP8 h, y (fp32).
+struct MxMoeLayout {
+    RouteLayout r;
+    size_t perm, inv, plan, xq, xs, h, hmax, hq, hs, y, end;
+};
+
+MxMoeLayout mx_moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
+{
+    MxMoeLayout L{};
+    const int64_t np = T * k;
+    L.r = route_layout(np, E);
+    size_t o = L.r.end;
+    L.perm = o; o = align256(o + sizeof(int32_t) * np);
+    L.inv = o; o = align256(o + sizeof(int32_t) * np);
+    L.plan = o; o = align256(o + sizeof(int32_t) * 12 * (E + 1));
+    L.xq = o; o = align256(o + (size_t)(T * H));
+    L.xs = o; o = align256(o + (size_t)(T * H / 32));
+    L.h = o; o = align256(o + sizeof(uint16_t) * (size_t)(np * I));
+    L.hmax = o; o = align256(o + sizeof(uint32_t));
+    L.hq = o; o = align256(o + (size_t)(np * I));
+    L.hs = o; o = align256(o + (size_t)(np * I / 32));
+    L.y = o; o = align256(o + sizeof(float) * (size_t)(np * H));
+    L.end = o;
+    return L;
+}
+
+template <int BM, int MODE>
+nvfp4_status launch_mx_grouped_class(MxArgs q, int64_t m_tiles_ub, hipStream_t st)
+{
+    q.m_tiles = m_tiles_ub;
+    const int64_t blocks = ceil_div(m_tiles_ub * q.n_tiles, 8) * 8;
+    if (blocks == 0)
+        return NVFP4_OK;
+    if (blocks > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    mx_w4a8_kernel<BM, 256, MODE><<<(unsigned)blocks, 256, 0, st>>>(q);
+    return launch_status();
+}
+
+// One grouped MX projection over the plan's classes: 256-row tiles, one
+// 128-row tile for a remainder of 65-128 rows, one 64-row tile for at most 64.
+template <int MODE>
+nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t total_rows, int32_t E, hipStream_t st)
+{
+    const int64_t E1 = E + 1;
+    p.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? 128 : 256);
+    auto cls = [&](int c) {
+        MxArgs q = p;
+        q.tile_off = plan + 3 * c * E1;
+        q.row_base = q.tile_off + E1;
+        q.row_lim = q.tile_off + 2 * E1;
+        return q;
+    };
+    nvfp4_status s = NVFP4_OK;
+    if (total_rows > 128)
+        s = launch_mx_grouped_class<256, MODE>(cls(0), total_rows / 128 + 1, st);
+    if (s == NVFP4_OK && total_rows > 64)
+        s = launch_mx_grouped_class<128, MODE>(cls(1), std::min<int64_t>(E, total_rows / 65 + 1), st);
+    if (s == NVFP4_OK)
+        s = launch_mx_grouped_class<64, MODE>(cls(3), std::min<int64_t>(E, total_rows), st);
+    return s;
+}
+
+// The two MX projections of a routed-expert layer over a tile plan that is
+// computed here (plan_ready false) or was already written.
+nvfp4_status mx_moe_gate_up_impl(const uint8_t* xq, const uint8_t* xe, const int32_t* perm, const int32_t* offsets,
+                                 int64_t T, int32_t k, int32_t E, int64_t H, int64_t I, const uint8_t* w13,
+                                 const uint8_t* w13e, void* h, uint32_t* h_amax, int32_t* plan, bool plan_ready,
+                                 hipStream_t st)
+{
+    if (!plan_ready) {
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, 0, plan);
+        nvfp4_status s = launch_status();
+        if (s != NVFP4_OK)
+            return s;
+    }
+    MxArgs p{};
+    p.a = xq;
+    p.a_sc = xe;
+    p.w = w13;
+    p.w_sc = w13e;
+    p.M = T * k;
+    p.N = I;
+    p.K = H;
+    p.perm = perm;
+    p.topk = k;
+    p.experts = E;
+    p.out = h;
+    p.h_amax = h_amax;
+    return mx_grouped<kModeGateUp>(p, plan, T * k, E, st);
+}
+
+nvfp4_status mx_moe_down_impl(const uint8_t* hq, const uint8_t* he, const int32_t* offsets, int64_t T, int32_t k,
+                              int32_t E, int64_t H, int64_t I, const uint8_t* w2, const uint8_t* w2e, float* y,
+                              int32_t* plan, bool plan_ready, hipStream_t st)
+{
+    if (!plan_ready) {
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, 0, plan);
+        nvfp4_status s = launch_status();
+        if (s != NVFP4_OK)
+            return s;
+    }
+    MxArgs q{};
+    q.a = hq;
+    q.a_sc = he;
+    q.w = w2;
+    q.w_sc = w2e;
+    q.M = T * k;
+    q.N = H;
+    q.K = I;
+    q.topk = k;
+    q.experts = E;
+    q.out = y;
+    return mx_grouped<kModeDown>(q, plan, T * k, E, st);
+}
+
+nvfp4_status mx_moe_check(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
+{
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF || H < 0 || I < 0)
+        return NVFP4_ERR_SHAPE;
+    if (H % 256 != 0 || I % 128 != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    return NVFP4_OK;
+}
+
 extern "C" {
 
 const char* nvfp4_status_string(nvfp4_status s)
@@ -546,6 +673,10 @@ size_t nvfp4_workspace_size(int op, int64_t T, int32_t k, int32_t E, int64_t H, 
         if (T < 0 || k < 1 || E < 1)
             return 0;
         return route_layout(T * k, E).end;
+    case NVFP4_OP_MX_MOE:
+        if (T < 0 || k < 1 || E < 1)
+            return 0;
+        return mx_moe_layout(T, k, E, H, I).end;
     }
     return 0;
 }
@@ -827,12 +958,103 @@ nvfp4_status mx_gemm_w4a8(const uint8_t* a, const uint8_t* a_e8m0, int64_t M, in
         const int64_t blocks = ceil_div(p.m_tiles * p.n_tiles, 8) * 8;
         if (blocks > 0x7FFFFFFF)
             return NVFP4_ERR_SHAPE;
-        mx_w4a8_kernel<256, 256><<<(unsigned)blocks, 256, 0, st>>>(p);
+        mx_w4a8_kernel<256, 256, kModeDense><<<(unsigned)blocks, 256, 0, st>>>(p);
     } else {
         p.m_tiles = ceil_div(M, 128);
         const int64_t blocks = ceil_div(p.m_tiles * p.n_tiles, 8) * 8;
-        mx_w4a8_kernel<128, 256><<<(unsigned)blocks, 256, 0, st>>>(p);
+        mx_w4a8_kernel<128, 256, kModeDense><<<(unsigned)blocks, 256, 0, st>>>(p);
     }
+    return launch_status();
+}
+
+nvfp4_status mx_moe_gate_up(const uint8_t* x_fp8, const uint8_t* x_e8m0, const int32_t* perm,
+                            const int32_t* offsets, int64_t T, int32_t k, int32_t E, int64_t H, int64_t I,
+                            const uint8_t* w13, const uint8_t* w13_e8m0, void* h_bf16, uint32_t* h_amax, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = mx_moe_check(T, k, E, H, I);
+    if (s != NVFP4_OK)
+        return s;
+    if (T == 0 || I == 0)
+        return NVFP4_OK;
+    if (!x_fp8 || !x_e8m0 || !perm || !offsets || !w13 || !w13_e8m0 || !h_bf16 || !h_amax || !ws ||
+        !aligned(x_fp8, 16) || !aligned(w13, 16) || !aligned(x_e8m0, 4) || !aligned(w13_e8m0, 4) ||
+        !aligned(h_bf16, 16) || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    const RouteLayout L = route_layout(T * k, E);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    return mx_moe_gate_up_impl(x_fp8, x_e8m0, perm, offsets, T, k, E, H, I, w13, w13_e8m0, h_bf16, h_amax,
+                               at<int32_t>(ws, L.plan_gu), false, S(stream));
+}
+
+nvfp4_status mx_moe_down(const uint8_t* h_fp8, const uint8_t* h_e8m0, const int32_t* offsets, int64_t T, int32_t k,
+                         int32_t E, int64_t H, int64_t I, const uint8_t* w2, const uint8_t* w2_e8m0, float* y,
+                         void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = mx_moe_check(T, k, E, H, I);
+    if (s != NVFP4_OK)
+        return s;
+    if (T == 0 || H == 0)
+        return NVFP4_OK;
+    if (!h_fp8 || !h_e8m0 || !offsets || !w2 || !w2_e8m0 || !y || !ws || !aligned(h_fp8, 16) || !aligned(w2, 16) ||
+        !aligned(h_e8m0, 4) || !aligned(w2_e8m0, 4) || !aligned(y, 16) || !aligned(ws, 256))
+        return NVFP4_ERR_INVALID_ARG;
+    const RouteLayout L = route_layout(T * k, E);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    return mx_moe_down_impl(h_fp8, h_e8m0, offsets, T, k, E, H, I, w2, w2_e8m0, y, at<int32_t>(ws, L.plan_dn),
+                            false, S(stream));
+}
+
+nvfp4_status mx_moe_w4a8(const void* x, const int32_t* ids, const float* w, int64_t T, int32_t k, int32_t E,
+                         int64_t H, int64_t I, const uint8_t* w13, const uint8_t* w13_e8m0, const uint8_t* w2,
+                         const uint8_t* w2_e8m0, void* out, void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = mx_moe_check(T, k, E, H, I);
+    if (s != NVFP4_OK)
+        return s;
+    if (T == 0 || H == 0)
+        return NVFP4_OK;
+    if (!x || !ids || !w || !w13 || !w13_e8m0 || !w2 || !w2_e8m0 || !out || !ws || !aligned(x, 16) ||
+        !aligned(out, 16) || !aligned(ws, 256) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13_e8m0, 4) ||
+        !aligned(w2_e8m0, 4))
+        return NVFP4_ERR_INVALID_ARG;
+    const MxMoeLayout L = mx_moe_layout(T, k, E, H, I);
+    if (ws_bytes < L.end)
+        return NVFP4_ERR_WORKSPACE;
+    hipStream_t st = S(stream);
+    const int64_t np = T * k;
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    int32_t* offsets = at<int32_t>(ws, L.r.offsets);
+    int32_t* plan = at<int32_t>(ws, L.plan);
+    uint32_t* hmax = at<uint32_t>(ws, L.hmax);
+    // 1. route (also zeroes the h max word); one tile plan serves both
+    // projections (64-row small tiles)
+    if ((s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st)) != NVFP4_OK)
+        return s;
+    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, 0, plan);
+    if ((s = launch_status()) != NVFP4_OK)
+        return s;
+    // 2. x -> MXFP8 (token order)
+    if ((s = mxfp8_quantize(x, T, H, H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), stream)) != NVFP4_OK)
+        return s;
+    // 3. gate_up + SwiGLU (h bf16, list order)
+    if ((s = mx_moe_gate_up_impl(at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), perm, offsets, T, k, E, H, I, w13,
+                                 w13_e8m0, at<void>(ws, L.h), hmax, plan, true, st)) != NVFP4_OK)
+        return s;
+    // 4. h -> MXFP8 (list order)
+    if ((s = mxfp8_quantize(at<void>(ws, L.h), np, I, I, at<uint8_t>(ws, L.hq), at<uint8_t>(ws, L.hs), stream)) !=
+        NVFP4_OK)
+        return s;
+    // 5. down (y fp32, list order)
+    if ((s = mx_moe_down_impl(at<uint8_t>(ws, L.hq), at<uint8_t>(ws, L.hs), offsets, T, k, E, H, I, w2, w2_e8m0,
+                              at<float>(ws, L.y), plan, true, st)) != NVFP4_OK)
+        return s;
+    // 6. router-weighted combine
+    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(at<float>(ws, L.y), inv, w, T, k, H, 1, 0,
+                                                                   (u32x2*)out);
     return launch_status();
 }
 

@@ -109,12 +109,20 @@ mxfp8_encode_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t blocks_pe
 struct MxArgs {
     const uint8_t* a;      // E4M3 [M, K]
     const uint8_t* a_sc;   // UE8M0 [M, K/32]
-    const uint8_t* w;      // E2M1 packed [N, K/2]
-    const uint8_t* w_sc;   // UE8M0 [N, K/32]
-    int64_t M, N, K;
+    const uint8_t* w;      // E2M1 packed [experts][N_w, K/2]
+    const uint8_t* w_sc;   // UE8M0 [experts][N_w, K/32]
+    int64_t M, N, K;       // gate_up: N = I (W holds 2I rows: gate, then up)
     int64_t m_tiles, n_tiles;
-    void* out;             // [M, N] fp32 or bf16
+    void* out;             // dense: [M, N] fp32 or bf16; gate_up: h bf16; down: y fp32
     int out_bf16;
+    // grouped projections: the tile plan of one class, as GemmArgs has it
+    const int32_t* tile_off;
+    const int32_t* row_base;
+    const int32_t* row_lim;
+    const int32_t* perm;   // gate_up: list position -> t*k + j
+    int32_t topk;
+    int32_t experts;
+    uint32_t* h_amax;      // gate_up: max |h| bits (atomic)
 };
 
 constexpr int kMxGrpK = 128;  // K elements per staged group (two MFMA k-steps)
@@ -125,7 +133,7 @@ constexpr int kMxGrpK = 128;  // K elements per staged group (two MFMA k-steps)
 // paired-row layout tpos) into one of three buffers with the LDS DMA path,
 // two groups ahead; the scale bytes (4 per row per group, one dword) are
 // loaded straight into registers one group ahead.  One barrier per group.
-template <int BM, int BN>
+template <int BM, int BN, int MODE>
 __global__ void __launch_bounds__(256)
 mx_w4a8_kernel(MxArgs p)
 {
@@ -154,15 +162,36 @@ mx_w4a8_kernel(MxArgs p)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_m = wave / WN, wave_n = wave % WN;
-    const int64_t bid = xcd_item(p.m_tiles * p.n_tiles);
-    if (bid < 0)
+    // tile coordinates, A rows and W rows through the grouped-GEMM helpers
+    // (dense: the plain tiling); MX operands carry no global scale
+    GemmArgs g{};
+    g.a_global = &kMxOne;
+    g.w_global = &kMxOne;
+    g.M = p.M;
+    g.N = p.N;
+    g.K = p.K;
+    g.m_tiles = p.m_tiles;
+    g.n_tiles = p.n_tiles;
+    g.tile_off = p.tile_off;
+    g.row_base = p.row_base;
+    g.row_lim = p.row_lim;
+    g.perm = p.perm;
+    g.topk = p.topk;
+    g.experts = p.experts;
+    g.out = p.out;
+    g.out_bf16 = p.out_bf16;
+    g.h_amax = p.h_amax;
+    g.ksplit = 1;
+    TileCoord tc;
+    if (!tile_coord<BM, MODE>(g, tc))
         return;
-    const int64_t mt = bid / p.n_tiles, nt = bid - mt * p.n_tiles;
-    const int64_t row0 = mt * BM, col0 = nt * BN;
     const int64_t K = p.K, kb = K / 32, kpb = K / 2;
     const int64_t ngr = K / kMxGrpK;
-    auto arow = [&](int r) -> int64_t { return row0 + r < p.M ? row0 + r : p.M - 1; };
-    auto wrow = [&](int r) -> int64_t { return col0 + r < p.N ? col0 + r : p.N - 1; };
+    const int64_t w_rows = MODE == kModeGateUp ? 2 * p.N : p.N;
+    const uint8_t* wexp = p.w + (int64_t)tc.e * w_rows * kpb;
+    const uint8_t* wsexp = p.w_sc + (int64_t)tc.e * w_rows * kb;
+    auto arow = [&](int r) -> int64_t { return tile_a_row<MODE>(g, tc, r); };
+    auto wrow = [&](int r) -> int64_t { return tile_w_row<BN, TN, MODE>(g, tc, r); };
 
     // copy sources: A copy j covers rows 8 (NJA wave + j) + lane / 8, lane
     // slot lane % 8 holding chunk (lane % 8) ^ (row % 8); W copy j as the
@@ -180,7 +209,7 @@ mx_w4a8_kernel(MxArgs p)
         const int q = 8 * (NJW * wave + j) + (lane >> 3);
         const int hc = (lane & 7) ^ ((q ^ (q >> 1)) & 7);
         const int r = 2 * q + (hc >> 2);
-        wsrc[j] = p.w + wrow(r) * kpb + 16 * (hc & 3);
+        wsrc[j] = wexp + wrow(r) * kpb + 16 * (hc & 3);
     }
     auto issue = [&](int64_t G, auto t) {
         const int64_t g = G < ngr ? G : ngr - 1;
@@ -207,7 +236,7 @@ mx_w4a8_kernel(MxArgs p)
         asc[i] = p.a_sc + arow(ra + 32 * i) * kb;
 #pragma unroll
     for (int j = 0; j < FN; j++)
-        wsc[j] = p.w_sc + wrow(rw + 32 * j) * kb;
+        wsc[j] = wsexp + wrow(rw + 32 * j) * kb;
     uint32_t sa[FM], sw[FN], na[FM], nw[FN];
     auto load_scales = [&](int64_t G, uint32_t (&da)[FM], uint32_t (&dw)[FN]) {
         const int64_t g = G < ngr ? G : ngr - 1;
@@ -315,22 +344,12 @@ mx_w4a8_kernel(MxArgs p)
     __syncthreads();
 
     // epilogue: the output tile staged per wave in the A buffers (free now)
-    // and written as 16-byte pieces
-    GemmArgs g{};
-    g.a_global = &kMxOne;
-    g.w_global = &kMxOne;
-    g.N = p.N;
-    g.M = p.M;
-    g.out = p.out;
-    g.out_bf16 = p.out_bf16;
-    TileCoord tc;
+    // and written as 16-byte pieces (gate_up: SwiGLU, h bf16 and its max;
+    // the scale of every expert is 1)
     tc.e = 0;
-    tc.row_begin = row0;
-    tc.row_end = row0 + BM < p.M ? row0 + BM : p.M;
-    tc.nt = nt;
     static_assert(2 * TM * 128 <= AB, "two waves' output staging fits one A buffer");
-    store_tile_t<BN, TM, TN, FM, FN, kModeDense>(g, tc, acc, wave_m, wave_n, lane,
-                                                 (wave < 2 ? lds_a0 : lds_a1) + (wave & 1) * TM * 128);
+    store_tile_t<BN, TM, TN, FM, FN, MODE>(g, tc, acc, wave_m, wave_n, lane,
+                                           (wave < 2 ? lds_a0 : lds_a1) + (wave & 1) * TM * 128);
 }
 
 }  // namespace nvfp4
