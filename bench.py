@@ -326,6 +326,18 @@ def decode_rows(dev, st, it):
     ms = time_loop(f, it, st)
     res["moe_384e_top8_w4a16_decode_T64"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(wbytes, ms),
                                              "frac_hbm": round(gbs(wbytes, ms) / PEAK_HBM_GBS, 4)}
+    # the same MXFP4 experts as an MX-native W4A8 layer (MXFP8 activations)
+    (m13, e13), (m2, e2) = W.mx13, W.mx2
+    mws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_MX_MOE, c4.T, c4.k, c4.E, c4.H, c4.I), dtype=torch.uint8,
+                      device=dev)
+    f = lambda: nv.mx_moe_w4a8(x, ids, wt, m13, e13, m2, e2, out=out, ws=mws)
+    f()
+    ms = time_loop(f, it, st)
+    mx_bytes = len(touched) * 3 * c4.H * c4.I * (0.5 + 1 / 32)
+    res["moe_384e_top8_mx_w4a8_decode_T64"] = {"ms": round(ms, 4), "touched_weight_GBps": gbs(mx_bytes, ms),
+                                               "frac_hbm": round(gbs(mx_bytes, ms) / PEAK_HBM_GBS, 4),
+                                               "bytes_basis": "touched MXFP4 experts: 0.5 + 1/32 B/elem"}
+    del mws
     p13, s13 = W.mx13
     dst = nv.NVFP4Tensor.empty(2 * c4.I, c4.H, c4.E, dev)
     rws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_REMAP, c4.E, 0, 0, 2 * c4.I, c4.H), dtype=torch.uint8, device=dev)
@@ -436,6 +448,28 @@ def breakdown(args):
     torch.cuda.empty_cache()
 
     res.update(decode_rows(dev, st, it))
+
+    # MX-native W4A8 layer on the 384-expert prefill batch (MXFP4 experts,
+    # MXFP8 activations on the scaled FP8 x FP4 MFMA)
+    cp = synth.C4_PREFILL
+    log("breakdown: MX W4A8 MoE prefill")
+    Wm = workloads.build_moe_weights(cp, dev, keep_mx=True)
+    del Wm.w13, Wm.w2
+    (m13, e13), (m2, e2) = Wm.mx13, Wm.mx2
+    xm = cp.x(dev)
+    idm, wtm = workloads.routing(cp, dev)
+    mws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_MX_MOE, cp.T, cp.k, cp.E, cp.H, cp.I), dtype=torch.uint8,
+                      device=dev)
+    outm = torch.empty((cp.T, cp.H), dtype=torch.bfloat16, device=dev)
+    f = lambda: nv.mx_moe_w4a8(xm, idm, wtm, m13, e13, m2, e2, out=outm, ws=mws)
+    f()
+    ms = time_loop(f, 5, st)
+    flops = 2.0 * cp.T * cp.k * 3 * cp.H * cp.I
+    res["moe_384e_top8_mx_w4a8_prefill_T16384"] = {
+        "ms": round(ms, 4), "TFLOPs": round(flops / ms / 1e9, 1), "frac_fp8_peak": round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+        "frac_f16_peak": round(flops / ms / 1e9 / PEAK_F16_TFLOPS, 4)}
+    del Wm, mws, outm, xm
+    torch.cuda.empty_cache()
 
     # KV cache 262144 x 4 x 256
     c5 = synth.C5
