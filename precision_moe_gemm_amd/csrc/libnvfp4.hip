@@ -536,10 +536,16 @@ nvfp4_status launch_mx_grouped_class(MxArgs q, int64_t m_tiles_ub, hipStream_t s
     return launch_status();
 }
 
+// Tile plan of the MX layer: 64-row small tiles; with at most 64 tokens
+// every row takes them (top-k sends a token to an expert at most once, so
+// no expert could fill a larger tile; any ids are still covered).
+int mx_all_small(int64_t T) { return T <= 64 ? 1 : 0; }
+
 // One grouped MX projection over the plan's classes: 256-row tiles, one
-// 128-row tile for a remainder of 65-128 rows, one 64-row tile for at most 64.
+// 128-row tile for a remainder of 65-128 rows, one 64-row tile for at most 64
+// (only the last when every row takes small tiles).
 template <int MODE>
-nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t total_rows, int32_t E, hipStream_t st)
+nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t T, int64_t total_rows, int32_t E, hipStream_t st)
 {
     const int64_t E1 = E + 1;
     p.n_tiles = ceil_div(p.N, MODE == kModeGateUp ? 128 : 256);
@@ -551,6 +557,8 @@ nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t total_rows, int32
         return q;
     };
     nvfp4_status s = NVFP4_OK;
+    if (mx_all_small(T))
+        return launch_mx_grouped_class<64, MODE>(cls(3), total_rows / 64 + std::min<int64_t>(E, total_rows), st);
     if (total_rows > 128)
         s = launch_mx_grouped_class<256, MODE>(cls(0), total_rows / 128 + 1, st);
     if (s == NVFP4_OK && total_rows > 64)
@@ -568,7 +576,7 @@ nvfp4_status mx_moe_gate_up_impl(const uint8_t* xq, const uint8_t* xe, const int
                                  hipStream_t st)
 {
     if (!plan_ready) {
-        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, 0, plan);
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, mx_all_small(T), plan);
         nvfp4_status s = launch_status();
         if (s != NVFP4_OK)
             return s;
@@ -586,7 +594,7 @@ nvfp4_status mx_moe_gate_up_impl(const uint8_t* xq, const uint8_t* xe, const int
     p.experts = E;
     p.out = h;
     p.h_amax = h_amax;
-    return mx_grouped<kModeGateUp>(p, plan, T * k, E, st);
+    return mx_grouped<kModeGateUp>(p, plan, T, T * k, E, st);
 }
 
 nvfp4_status mx_moe_down_impl(const uint8_t* hq, const uint8_t* he, const int32_t* offsets, int64_t T, int32_t k,
@@ -594,7 +602,7 @@ nvfp4_status mx_moe_down_impl(const uint8_t* hq, const uint8_t* he, const int32_
                               int32_t* plan, bool plan_ready, hipStream_t st)
 {
     if (!plan_ready) {
-        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, 0, plan);
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, mx_all_small(T), plan);
         nvfp4_status s = launch_status();
         if (s != NVFP4_OK)
             return s;
@@ -610,7 +618,7 @@ nvfp4_status mx_moe_down_impl(const uint8_t* hq, const uint8_t* he, const int32_
     q.topk = k;
     q.experts = E;
     q.out = y;
-    return mx_grouped<kModeDown>(q, plan, T * k, E, st);
+    return mx_grouped<kModeDown>(q, plan, T, T * k, E, st);
 }
 
 nvfp4_status mx_moe_check(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
@@ -1034,7 +1042,7 @@ nvfp4_status mx_moe_w4a8(const void* x, const int32_t* ids, const float* w, int6
     // projections (64-row small tiles)
     if ((s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st)) != NVFP4_OK)
         return s;
-    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, 0, plan);
+    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, mx_all_small(T), plan);
     if ((s = launch_status()) != NVFP4_OK)
         return s;
     // 2. x -> MXFP8 (token order)

@@ -34,12 +34,13 @@ def _mx_experts(cfg, which):
     return torch.stack(packed).contiguous(), torch.stack(e8).contiguous()
 
 
-def _check_mx_moe(orc, cfg, sample_rows=None, sample_tokens=None, seed=0):
+def _check_mx_moe(orc, cfg, sample_rows=None, sample_tokens=None, seed=0, ids=None):
     step(f"mx moe build E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} T={cfg.T}")
     w13p, w13e = _mx_experts(cfg, "w13")
     w2p, w2e = _mx_experts(cfg, "w2")
     x = cfg.x(DEV)
-    ids, w = workloads.routing(cfg, DEV)
+    rids, w = workloads.routing(cfg, DEV)
+    ids = rids if ids is None else ids.to(DEV)
     T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
     step("mx moe staged run")
     xq, xe = nv.mxfp8_quantize(x)
@@ -111,8 +112,16 @@ def test_mx_moe_all_tile_classes_sampled(orc):
 
 
 def test_mx_moe_decode_batch(orc):
-    """A decode-sized batch over many experts (one 64-row tile each)."""
+    """A decode-sized batch over many experts: every row in 64-row tiles."""
     _check_mx_moe(orc, synth.MoE(seed=52, E=64, k=8, H=512, I=256, T=16))
+
+
+def test_mx_moe_repeated_ids_decode_batch(orc):
+    """A small batch whose pairs all go to one expert (ids repeated within a
+    token): 120 rows of one expert in 64-row tiles, every row checked."""
+    cfg = synth.MoE(seed=53, E=4, k=3, H=256, I=128, T=40)
+    ids = torch.full((cfg.T, cfg.k), 2, dtype=torch.int32)
+    _check_mx_moe(orc, cfg, ids=ids)
 
 
 def test_mx_moe_unsupported_shapes():
