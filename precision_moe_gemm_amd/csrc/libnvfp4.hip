@@ -827,7 +827,9 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0, int64
     // 16 blocks per thread when every 16-block group is 16-byte aligned
     const int vec16 = per_mat % 16 == 0 && aligned(e8m0, 16) && aligned(out->scales, 16) && aligned(ws, 16);
     const int64_t items = vec16 ? per_mat / 16 : per_mat;
-    const unsigned parts2 = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, ceil_div(items, 256)));
+    // at most 32 workgroups per matrix: each reduces the matrix's partial
+    // exponent ranges once and then walks several groups
+    const unsigned parts2 = (unsigned)std::max<int64_t>(1, std::min<int64_t>(32, ceil_div(items, 256)));
     remap_scales_kernel<<<dim3(parts2, (unsigned)batch), kMxThreads, 0, S(stream)>>>(
         e8m0, flags, per_mat, pmax, pmin, (int)parts, (uint16_t*)out->scales, out->global, vec16);
     return launch_status();
