@@ -60,8 +60,16 @@ nvfp4_status launch_quantize(QuantArgs a, int ntensors, hipStream_t st)
     const int64_t nblk = a.rows * a.blocks_per_row;
     if (nblk == 0)
         return NVFP4_OK;
-    dim3 grid(stream_grid(ceil_div(2 * nblk, 8), 4096), ntensors);  // 8 half-blocks per thread per trip
-    quantize_kernel<<<grid, kQuantThreads, 0, st>>>(a);
+    // 8 half-blocks per thread per trip; 2 when that leaves under 4
+    // workgroups per CU (a KV-cache chunk)
+    const int64_t wg8 = ceil_div(2 * nblk, 8 * kQuantThreads) * ntensors;
+    if (wg8 < 1024) {
+        dim3 grid(stream_grid(ceil_div(2 * nblk, 2), 4096), ntensors);
+        quantize_kernel<2><<<grid, kQuantThreads, 0, st>>>(a);
+    } else {
+        dim3 grid(stream_grid(ceil_div(2 * nblk, 8), 4096), ntensors);
+        quantize_kernel<8><<<grid, kQuantThreads, 0, st>>>(a);
+    }
     return launch_status();
 }
 
@@ -96,7 +104,7 @@ nvfp4_status quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld
         // still publish G (1 for an empty dynamic tensor, or the static value)
         a.rows = 1;
         a.blocks_per_row = 0;
-        quantize_kernel<<<dim3(1, 1), kQuantThreads, 0, st>>>(a);
+        quantize_kernel<8><<<dim3(1, 1), kQuantThreads, 0, st>>>(a);
         return launch_status();
     }
     return launch_quantize(a, 1, st);

@@ -82,6 +82,7 @@ struct QuantArgs {
     int nparts;
 };
 
+template <int kQU>
 __global__ void __launch_bounds__(kQuantThreads)
 quantize_kernel(QuantArgs a)
 {
@@ -97,8 +98,8 @@ quantize_kernel(QuantArgs a)
     // 2j+1 hold the two halves of a block and share its max with one lane
     // swap, so loads and code stores are contiguous per instruction.  A
     // workgroup takes kQU * 256 consecutive half-blocks per trip, all loads
-    // issued first.
-    constexpr int kQU = 8;
+    // issued first (kQU = 8; 2 for launches too small to fill the chip, so
+    // that four times as many waves share the work).
     constexpr int64_t kChunk = (int64_t)kQU * kQuantThreads;
     u32x4 v[kQU];
     auto load_trip = [&](int64_t base) {
