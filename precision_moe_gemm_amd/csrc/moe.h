@@ -228,9 +228,12 @@ NVFP4_DEV void plan_block(const int32_t* offs, int E, int small_bm, int all_smal
         cnt2 += plan_class<2>(lo, hi, small_bm, all_small).tiles;
         cnt3 += plan_class<3>(lo, hi, small_bm, all_small).tiles;
     }
-    const ScanResult s0 = block_exclusive_scan(cnt0, lds16);
-    const ScanResult s1 = block_exclusive_scan(cnt1, lds16);
-    const ScanResult s2 = block_exclusive_scan(cnt2, lds16);
+    // when every row takes small tiles the other classes are empty: their
+    // counts are zero in every thread, so their scans are skipped
+    const ScanResult zero{0, 0};
+    const ScanResult s0 = all_small ? zero : block_exclusive_scan(cnt0, lds16);
+    const ScanResult s1 = all_small ? zero : block_exclusive_scan(cnt1, lds16);
+    const ScanResult s2 = all_small ? zero : block_exclusive_scan(cnt2, lds16);
     const ScanResult s3 = block_exclusive_scan(cnt3, lds16);
     int32_t run0 = s0.prefix, run1 = s1.prefix, run2 = s2.prefix, run3 = s3.prefix;
     auto put = [&](int c, int e, const ClassPlan& cp, int32_t& run) {
