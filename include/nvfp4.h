@@ -33,8 +33,10 @@
  *     out of range) set a sticky per-device error word that
  *     nvfp4_get_error() reads and clears.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified output.
- *   - The library keeps no mutable host state; calls on different streams
- *     may run concurrently as long as their buffers do not overlap.
+ *   - The only host state is a per-device cache of occupancy queries,
+ *     written with relaxed atomics (every thread computes the same value);
+ *     calls on different streams may run concurrently as long as their
+ *     buffers do not overlap.
  *
  * Arithmetic (bit-exact contract).  Quantization follows these fp32 steps,
  * each IEEE round-to-nearest-even, no fused multiply-add:
@@ -63,9 +65,13 @@ typedef enum {
     NVFP4_ERR_RANGE = 3,       /* data outside what the format can hold      */
     NVFP4_ERR_WORKSPACE = 4,   /* ws too small                               */
     NVFP4_ERR_DEVICE = 5,      /* a HIP runtime error (launch, no device)    */
-    NVFP4_ERR_UNSUPPORTED = 6  /* a valid request this build does not handle */
+    NVFP4_ERR_UNSUPPORTED = 6, /* a valid request this build does not handle */
+    NVFP4_ERR_DATA = 7         /* (checks on) non-finite input, NaN or negative
+                                  block scale, global not finite and positive */
 } nvfp4_status;
 
+/* Output element types.  Entry points take them as int32_t, so that any value
+ * a C caller passes is well defined to check (others: NVFP4_ERR_INVALID_ARG). */
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
 
 /* One NVFP4 tensor, or `batch` tensors of the same shape stacked
@@ -132,7 +138,7 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int6
  * (page "DeepSeek-V4.1-Flash-NVFP4", section 二: value = code x block scale
  * x tensor scale).
  */
-nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dtype, void* stream);
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, int32_t dtype, void* stream);
 
 /*
  * Row gather-dequantize for NVFP4 embedding tables (page
@@ -145,7 +151,7 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dty
  * returns OK).  n * cols / 8 must stay below 2^32 (else UNSUPPORTED).
  */
 nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* ids, int64_t n,
-                                     void* out, nvfp4_dtype dtype, void* stream);
+                                     void* out, int32_t dtype, void* stream);
 
 /*
  * MXFP4 encode (OCP MX: blocks of 32 along the last dimension, UE8M0 scale
@@ -186,7 +192,8 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0,
  *   C[m, n] = G_A * G_W * sum_k (e2m1*s)(A[m,k]) * (e2m1*s)(W[n,k])
  * A: [M, K] (batch 1), W: [N, K] (batch 1); C: [M, N] row-major, fp32 or
  * bf16.  Products are exact; the sum is accumulated in fp32.
- * K % 16 == 0 (K % 64 == 0 on this build, else NVFP4_ERR_UNSUPPORTED).
+ * K % 16 == 0 (a K that is not a multiple of 64 runs a slower kernel that
+ * reads the last, partial 64-element stage block by block).
  * ws: nvfp4_workspace_size(NVFP4_OP_GEMM, M, 0, 0, K, N) bytes, 256-byte
  *     aligned, holding the fp32 partial sums of few-row shapes whose K is
  *     split over several workgroups (they are added in a fixed order, so
@@ -194,7 +201,7 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0,
  *     GEMM then runs unsplit, slower for such shapes.  A non-NULL ws that is
  *     smaller than required gives NVFP4_ERR_WORKSPACE.
  */
-nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, nvfp4_dtype dtype,
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, int32_t dtype,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -227,7 +234,7 @@ nvfp4_status mxfp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, int6
  * the scale arrays 4-byte aligned.
  */
 nvfp4_status mx_gemm_w4a8(const uint8_t* a_fp8, const uint8_t* a_e8m0, int64_t M, int64_t K,
-                          const uint8_t* w_packed, const uint8_t* w_e8m0, int64_t N, void* C, nvfp4_dtype dtype,
+                          const uint8_t* w_packed, const uint8_t* w_e8m0, int64_t N, void* C, int32_t dtype,
                           void* stream);
 
 /*
@@ -286,7 +293,7 @@ nvfp4_status mx_moe_w4a8(const void* x_bf16, const int32_t* topk_ids, const floa
  * (NVFP4_OP_GEMM, M, 0, 0, K, N) bytes, or NULL).
  */
 nvfp4_status nvfp4_gemm_w4a16(const void* a_bf16, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
-                              void* C, nvfp4_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+                              void* C, int32_t dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * W4A16 routed-expert MoE layer (page "Qwen3.8-Flash-Next-FP4-Local",
@@ -322,7 +329,8 @@ nvfp4_status nvfp4_moe_w4a16(const void* x_bf16, const int32_t* topk_ids, const 
  * the pair is dropped); topk_w fp32 [T, k]; x bf16 [T, H] contiguous;
  * w13: batch E, rows 2I, cols H; w2: batch E, rows H, cols I;
  * static_in_globals: device float[2] or NULL; out bf16 [T, H].
- * H % 64 == 0 and I % 128 == 0 on this build (else NVFP4_ERR_UNSUPPORTED).
+ * H % 16 == 0 and I % 16 == 0 (else NVFP4_ERR_SHAPE); H % 64 != 0 or
+ * I % 128 != 0 runs every row in slower 32-row tiles.
  * ws: nvfp4_workspace_size(NVFP4_OP_MOE, T, k, E, H, I) bytes.
  */
 nvfp4_status nvfp4_moe_grouped_gemm(const void* x_bf16, const int32_t* topk_ids,
@@ -405,7 +413,7 @@ nvfp4_status nvfp4_kv_quant(const void* k_bf16, const void* v_bf16, int64_t n, i
  * ([n, heads, head_dim], fp32 or bf16); either may be NULL to skip it. */
 nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache,
                               int64_t heads, int64_t tok_begin, int64_t n, void* k_out,
-                              void* v_out, nvfp4_dtype dtype, void* stream);
+                              void* v_out, int32_t dtype, void* stream);
 
 /*
  * Scale audit (page "Qwen3.8-Flash-Next-NVFP4", section 证据链: every block
@@ -420,12 +428,30 @@ nvfp4_status nvfp4_audit_scales(const nvfp4_tensor* t, int64_t* counts_out, void
  * since the last call. */
 nvfp4_status nvfp4_get_error(void* stream);
 
-/* Static description of a status code. */
-const char* nvfp4_status_string(nvfp4_status s);
+/* Static description of a status code (any int32_t; unknown codes give
+ * "unknown status"). */
+const char* nvfp4_status_string(int32_t s);
 
 /* Format constants, host: block size 16, E2M1 exponent/mantissa bits 2/1,
  * E4M3 exponent/mantissa bits 4/3, effective bits x 100 (450). */
 void nvfp4_recipe(int32_t out[6]);
+
+/* Data checks (the release audit of page "Qwen3.8-Flash-Next-NVFP4", section
+ * 证据链, applied to every call): while on, the quantize, dequantize, GEMM
+ * and routed-expert entry points first launch checks of their operands --
+ * bf16 inputs finite, every E4M3 block scale neither a NaN pattern nor
+ * negative, every fp32 global finite and positive -- that raise the sticky
+ * NVFP4_ERR_DATA (read with nvfp4_get_error); the computation still runs.
+ * Expert ids are always checked (NVFP4_ERR_RANGE).  Off by default; on when
+ * the library was built with -DNVFP4_CHECK=1 or the environment variable
+ * NVFP4_CHECK is 1 when the library is loaded.  Host: sets the switch for
+ * the process (on != 0), returns the previous setting. */
+int nvfp4_set_checks(int on);
+
+/* Host: a hash of the sources and flags this library was built from (16 hex
+ * digits, static storage).  Loaders compare it with their source tree and
+ * refuse a stale build. */
+const char* nvfp4_build_stamp(void);
 
 #ifdef __cplusplus
 }

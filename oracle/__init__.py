@@ -30,7 +30,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libnvfp4_oracle.so")
+# NVFP4_ORACLE_LIB selects another build of nvfp4_oracle.c (the sanitizer
+# build used by the CPU tests)
+_LIB_PATH = os.environ.get("NVFP4_ORACLE_LIB") or os.path.join(_HERE, "libnvfp4_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -53,6 +55,23 @@ def build(force: bool = True) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized(out: str) -> str:
+    """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc; load it with gcc's libasan preloaded, see sanitizer_runtime)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def sanitizer_runtime() -> str:
+    return subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                          check=True).stdout.strip()
 
 
 def _load():

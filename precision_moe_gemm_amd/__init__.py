@@ -23,7 +23,7 @@ __all__ = [
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
     "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8", "mx_moe_w4a8", "mx_moe_gate_up", "mx_moe_down",
-    "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error",
+    "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error", "nvfp4_set_checks",
     "nvfp4_recipe", "status_string",
 ]
 
@@ -452,6 +452,12 @@ def nvfp4_audit_scales(t: NVFP4Tensor) -> torch.Tensor:
     _check(_lib.load().nvfp4_audit_scales(ctypes.byref(tc), _ptr(counts), _stream(t.device)),
            "nvfp4_audit_scales")
     return counts
+
+
+def nvfp4_set_checks(on: bool) -> bool:
+    """Switch the operand data checks on or off for the process (see
+    include/nvfp4.h); returns the previous setting."""
+    return bool(_lib.load().nvfp4_set_checks(1 if on else 0))
 
 
 def nvfp4_get_error(device=None) -> int:

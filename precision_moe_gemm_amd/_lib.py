@@ -10,12 +10,14 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+# NVFP4_LIB_PATH selects another build of the same sources (the sanitizer
+# build of the host layer); it must carry the same source stamp
+LIB_PATH = os.environ.get("NVFP4_LIB_PATH") or os.path.join(HERE, "libnvfp4.so")
 
 _lock = threading.Lock()
 _lib = None
 
-OK, INVALID_ARG, SHAPE, RANGE, WORKSPACE, DEVICE, UNSUPPORTED = range(7)
+OK, INVALID_ARG, SHAPE, RANGE, WORKSPACE, DEVICE, UNSUPPORTED, DATA = range(8)
 F32, BF16 = 0, 1
 OP_QUANTIZE, OP_REMAP, OP_GEMM, OP_MOE, OP_MOE_ROUTE, OP_MX_MOE = range(6)
 
@@ -70,6 +72,8 @@ SIGNATURES = {
     "nvfp4_get_error": (ST, [P]),
     "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4_recipe": (None, [ctypes.POINTER(ctypes.c_int32)]),
+    "nvfp4_build_stamp": (ctypes.c_char_p, []),
+    "nvfp4_set_checks": (ctypes.c_int, [ctypes.c_int]),
 }
 
 
@@ -84,6 +88,14 @@ def load():
                 f"libnvfp4.so not found at {LIB_PATH}; build it with "
                 "`python -m precision_moe_gemm_amd.build` (there is no fallback path)")
         lib = ctypes.CDLL(LIB_PATH)
+        from .build import source_hash
+        lib.nvfp4_build_stamp.restype = ctypes.c_char_p
+        lib.nvfp4_build_stamp.argtypes = []
+        stamp, want = lib.nvfp4_build_stamp().decode(), source_hash()
+        if stamp != want:
+            raise ImportError(
+                f"libnvfp4.so at {LIB_PATH} was built from other sources (stamp {stamp}, sources {want}); "
+                "rebuild it with `python -m precision_moe_gemm_amd.build`")
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype = res

@@ -257,9 +257,13 @@ template <int BN, int TN, int MODE>
 NVFP4_DEV int64_t tile_w_row(const GemmArgs& p, const TileCoord& tc, int r)
 {
     if (MODE == kModeGateUp) {
+        // columns past N (a last tile of an N that is not a multiple of the
+        // tile) reread column N - 1 of the same half and are never stored
         const int wn = r / TN, rr = r % TN;
         const int64_t base = tc.nt * (BN / 2) + wn * (TN / 2);
-        return rr < TN / 2 ? base + rr : p.N + base + (rr - TN / 2);
+        int64_t c = base + (rr < TN / 2 ? rr : rr - TN / 2);
+        c = c < p.N ? c : p.N - 1;
+        return rr < TN / 2 ? c : p.N + c;
     }
     const int64_t n = tc.nt * BN + r;
     return n < p.N ? n : p.N - 1;
@@ -308,7 +312,7 @@ NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&ac
             for (int b = threadIdx.x; b < TM * (HC / 16); b += blockDim.x) {
                 const int row = b / (HC / 16), bc = b - row * (HC / 16);
                 const int64_t grow = tc.row_begin + pm * TM + row;
-                if (grow < tc.row_end) {
+                if (grow < tc.row_end && hcol0 + 16 * bc < p.N) {
                     const u32x4 v0 = *(const u32x4*)(hs + row * HC + 16 * bc);
                     const u32x4 v1 = *(const u32x4*)(hs + row * HC + 16 * bc + 8);
                     const uint32_t a0 = absmax_bits8(v0), a1 = absmax_bits8(v1);
@@ -333,6 +337,8 @@ NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&ac
                 if (rr < rows_left) {
 #pragma unroll
                     for (int j = 0; j < FN / 2; j++) {
+                        if (col0 + j * 32 >= p.N)
+                            continue;
                         const float gg = acc[i][j][r] * gscale;
                         const float uu = acc[i][j + FN / 2][r] * gscale;
                         const uint16_t hb = f32_to_bf16(silu_f(gg) * uu);
@@ -373,7 +379,12 @@ NVFP4_DEV void store_tile(const GemmArgs& p, const TileCoord& tc, float16_t (&ac
     }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+// RAG: K is a multiple of 16 but not of 64.  Rows then start on 8-byte
+// (codes) and 1-byte (scales) boundaries, so codes are loaded 8 bytes (one
+// 16-element block) at a time and scale bytes one at a time, and the last,
+// partial stage reads only its valid blocks: the rest of it is zero codes
+// with zero scales, which add nothing to the sums.
+template <int BM, int BN, int WM, int WN, int MODE, bool RAG = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(GemmArgs p)
 {
@@ -432,8 +443,23 @@ gemm_kernel(GemmArgs p)
         }
     }
     u32x4 creg[2][RPT][2];
-    const int64_t nstages = K / kBK;
+    const int64_t nstages = RAG ? (K + kBK - 1) / kBK : K / kBK;
     auto load_stage = [&](int st, int set) {
+        if (RAG) {
+            // valid code bytes of this stage: 32, or 8/16/24 in the last one
+            const int64_t vb = kpb - (int64_t)st * kStageCodeBytes;
+#pragma unroll
+            for (int i = 0; i < RPT; i++) {
+                const uint8_t* c = csrc[i] + (int64_t)st * kStageCodeBytes;
+                u32x2 v[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    v[q] = 8 * q < vb ? *(const u32x2*)(c + 8 * q) : (u32x2){0, 0};
+                creg[set][i][0] = (u32x4){v[0].x, v[0].y, v[1].x, v[1].y};
+                creg[set][i][1] = (u32x4){v[2].x, v[2].y, v[3].x, v[3].y};
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < RPT; i++) {
             const u32x4* c = (const u32x4*)(csrc[i] + st * kStageCodeBytes);
@@ -443,9 +469,28 @@ gemm_kernel(GemmArgs p)
     };
     // scale dwords of stages [4 G, 4 G + 4): one 16-byte load per row, or,
     // for a last group that is not whole, one clamped dword per stage
+    // (ragged K: byte loads, zero past the row's kpsb bytes)
     u32x4 tsc[RPT];
     auto load_scales = [&](int64_t grp) {
         const int64_t st0 = 4 * grp;
+        if (RAG) {
+            const int64_t last = nstages - 1;
+#pragma unroll
+            for (int i = 0; i < RPT; i++) {
+                uint32_t d[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int64_t b0 = (st0 + j < last ? st0 + j : last) * kStageScaleBytes;
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; b++)
+                        w |= (b0 + b < kpsb ? (uint32_t)ssrc[i][b0 + b] : 0u) << (8 * b);
+                    d[j] = w;
+                }
+                tsc[i] = (u32x4){d[0], d[1], d[2], d[3]};
+            }
+            return;
+        }
         if (st0 + 4 <= nstages) {
 #pragma unroll
             for (int i = 0; i < RPT; i++)

@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 
 #include "common.h"
 #include "gemm.h"
@@ -12,6 +15,10 @@
 #include "mx.h"
 #include "mx8.h"
 #include "quant.h"
+
+#ifndef NVFP4_BUILD_STAMP
+#define NVFP4_BUILD_STAMP "unstamped"
+#endif
 
 using namespace nvfp4;
 
@@ -52,6 +59,52 @@ nvfp4_status check_tensor(const nvfp4_tensor* t, bool need_global = true)
         return NVFP4_ERR_INVALID_ARG;
     return NVFP4_OK;
 }
+
+// ---------------------------------------------------------------- checks
+// The data-check switch (nvfp4_set_checks): its start value comes from the
+// NVFP4_CHECK environment variable when the library is loaded, else from the
+// NVFP4_CHECK build flag.
+#ifndef NVFP4_CHECK
+#define NVFP4_CHECK 0
+#endif
+int checks_initial()
+{
+    const char* e = getenv("NVFP4_CHECK");
+    if (e && *e)
+        return atoi(e) != 0;
+    return NVFP4_CHECK != 0;
+}
+std::atomic<int> g_checks{checks_initial()};
+bool checks_on() { return g_checks.load(std::memory_order_relaxed) != 0; }
+
+void check_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld, hipStream_t st)
+{
+    if (rows > 0 && cols > 0)
+        check_bf16_kernel<<<stream_grid(rows * cols, 2048), kQuantThreads, 0, st>>>((const uint16_t*)x, rows, cols,
+                                                                                     ld);
+}
+
+void check_globals(const float* g, int64_t n, hipStream_t st)
+{
+    if (g && n > 0)
+        check_globals_kernel<<<1, 64, 0, st>>>(g, n);
+}
+
+// scale bytes and globals of validated tensors (null entries skipped)
+nvfp4_status check_tensors_data(std::initializer_list<const nvfp4_tensor*> ts, hipStream_t st)
+{
+    for (const nvfp4_tensor* t : ts) {
+        if (!t)
+            continue;
+        const int64_t n = t->batch * t->rows * (t->cols / 16);
+        if (n > 0)
+            check_scales_kernel<<<stream_grid(n, 2048), kQuantThreads, 0, st>>>(t->scales, n);
+        check_globals(t->global, t->batch, st);
+    }
+    return launch_status();
+}
+
+nvfp4_status check_tensor_data(const nvfp4_tensor* t, hipStream_t st) { return check_tensors_data({t}, st); }
 
 // ---------------------------------------------------------------- quantize
 // Launch the block quantizer for up to two tensors sharing a shape.
@@ -111,7 +164,7 @@ nvfp4_status quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld
 }
 
 // ---------------------------------------------------------------- GEMM
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, bool RAG = false>
 nvfp4_status launch_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
 {
     p.m_tiles = m_tiles_ub;
@@ -121,7 +174,7 @@ nvfp4_status launch_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     blocks = ceil_div(blocks, 8) * 8;
     if (blocks > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    gemm_kernel<BM, BN, WM, WN, MODE><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(p);
+    gemm_kernel<BM, BN, WM, WN, MODE, RAG><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(p);
     return launch_status();
 }
 
@@ -181,14 +234,17 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K)
 
 // Workgroups of a weight-streaming kernel that the current device holds at
 // once, rounded down to a multiple of 8 (one query per kernel and device).
+// The per-device cache is atomic (relaxed): threads that race on a first
+// call each compute the same value and store it.
 template <int MODE, bool P2, bool A16, int BM>
 int64_t stream_resident()
 {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         dev = 0;
-    if (cached[dev] == 0) {
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_stream_kernel<MODE, P2, A16, BM>, kSkThreads, 0) !=
                 hipSuccess ||
@@ -196,9 +252,10 @@ int64_t stream_resident()
             per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 8;
-        cached[dev] = std::max(8, per_cu * cus / 8 * 8);
+        v = std::max(8, per_cu * cus / 8 * 8);
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 template <int MODE, bool P2, bool A16, int BM>
@@ -269,6 +326,12 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
     }
     p.ksplit = 1;
     p.n_tiles = ceil_div(p.N, 256);
+    if (p.K % kBK != 0) {
+        // K a multiple of 16 only: the register-decode kernel with ragged loads
+        if (p.M > 32)
+            return launch_gemm<64, 256, 1, 4, kModeDense, true>(p, ceil_div(p.M, 64), st);
+        return launch_gemm<32, 256, 1, 4, kModeDense, true>(p, ceil_div(p.M, 32), st);
+    }
     if (p.M >= 256)
         return launch_tile<256, 256, kModeDense>(p, ceil_div(p.M, 256), st);
     if (p.M >= 96)
@@ -276,6 +339,15 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
     if (p.M > 32)
         return launch_gemm<64, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 64), st);
     return launch_gemm<32, 256, 1, 4, kModeDense>(p, ceil_div(p.M, 32), st);
+}
+
+// A grouped projection whose K is not a multiple of the 64-element stage, or
+// a gate_up projection whose N (= I) is not a multiple of its 128-column
+// tile, runs every row in 32-row tiles of the register-decode kernel (ragged
+// K loads, columns past N masked).
+bool grouped_ragged(int mode, int64_t K, int64_t N)
+{
+    return K % kBK != 0 || (mode == kModeGateUp && N % 128 != 0);
 }
 
 // Rows of the small tiles of a grouped projection with reduction length K
@@ -286,9 +358,9 @@ nvfp4_status dispatch_dense(GemmArgs p, hipStream_t st)
 // then read once), and of 16 rows otherwise.  (Measured: 32-row streaming
 // tiles run slower for the remainders next to the 128- and 256-row tiles and
 // for skewed decode batches, where most experts hold a few rows.)
-int grouped_small_bm(int64_t K, int all_small, int64_t rows, int32_t experts)
+int grouped_small_bm(int64_t K, int all_small, int64_t rows, int32_t experts, bool ragged = false)
 {
-    if (K % kSkBK != 0)
+    if (ragged || K % kSkBK != 0)
         return 32;
     return (all_small && rows >= 2 * kSkBM * (int64_t)experts) ? 2 * kSkBM : kSkBM;
 }
@@ -324,7 +396,7 @@ int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 int moe_gate_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 {
     const int64_t np = T * k;
-    if (np <= 0 || np > 256 || H % kSkBK != 0)
+    if (np <= 0 || np > 256 || H % kSkBK != 0 || grouped_ragged(kModeGateUp, H, I))
         return 1;
     const int bm = grouped_small_bm(H, 1, np, E);
     const int64_t tiles = small_tiles_est(np, E, bm) * ceil_div(I, kSkBN / 2);
@@ -345,8 +417,10 @@ int moe_gate_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 // top-k routing sends a token to an expert at most once, so no expert can
 // fill a 128- or 256-row tile and those launches would be empty.  (Any ids
 // still come out right: small tiles cover every row of every expert.)
-int grouped_all_small(int64_t T, int64_t K, int ksplit)
+int grouped_all_small(int64_t T, int64_t K, int ksplit, bool ragged = false)
 {
+    if (ragged)
+        return 1;
     if (K % kSkBK != 0)
         return 0;
     return (ksplit > 1 || T <= 64) ? 1 : 0;
@@ -356,14 +430,15 @@ template <int MODE>
 nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_rows, int experts,
                               int all_small, int32_t* plan, bool plan_ready, hipStream_t st)
 {
-    const bool stream_ok = p.K % kSkBK == 0;
+    const bool ragged = grouped_ragged(MODE, p.K, p.N);
+    const bool stream_ok = !ragged && p.K % kSkBK == 0;
     if (p.a_bf16 && !stream_ok)
         return NVFP4_ERR_UNSUPPORTED;
     if (p.ksplit < 1 || !stream_ok)
         p.ksplit = 1;
-    if (p.ksplit > 1 || p.a_bf16)
+    if (p.ksplit > 1 || p.a_bf16 || ragged)
         all_small = 1;  // the split planes cover every row; W4A16 streams every tile
-    const int small_bm = grouped_small_bm(p.K, all_small, total_rows, experts);
+    const int small_bm = grouped_small_bm(p.K, all_small, total_rows, experts, ragged);
     nvfp4_status s = NVFP4_OK;
     if (!plan_ready) {
         moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, experts, small_bm, all_small, plan);
@@ -398,8 +473,8 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
         if (s != NVFP4_OK)
             return s;
     }
-    GemmArgs q = cls(3);
-    // class 3: every tile holds at least one row; at most 64 rows per expert
+    GemmArgs q = cls(kPlanSmall);
+    // small class: every tile holds at least one row; at most 64 rows per expert
     // (4 tiles of 16 or 2 of 32) unless all rows take small tiles, then at
     // most one partial tile per non-empty expert
     const int64_t m_small =
@@ -411,6 +486,8 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
     }
     q.ksplit = 1;
     q.n_tiles = ceil_div(p.N, big_cols);
+    if (p.K % kBK != 0)
+        return launch_gemm<32, 256, 1, 4, MODE, true>(q, m_small, st);
     return launch_gemm<32, 256, 1, 4, MODE>(q, m_small, st);
 }
 
@@ -519,7 +596,7 @@ MxMoeLayout mx_moe_layout(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
     size_t o = L.r.end;
     L.perm = o; o = align256(o + sizeof(int32_t) * np);
     L.inv = o; o = align256(o + sizeof(int32_t) * np);
-    L.plan = o; o = align256(o + sizeof(int32_t) * 12 * (E + 1));
+    L.plan = o; o = align256(o + sizeof(int32_t) * 3 * kPlanClasses * (E + 1));
     L.xq = o; o = align256(o + (size_t)(T * H));
     L.xs = o; o = align256(o + (size_t)(T * H / 32));
     L.h = o; o = align256(o + sizeof(uint16_t) * (size_t)(np * I));
@@ -566,13 +643,13 @@ nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t T, int64_t total_
     };
     nvfp4_status s = NVFP4_OK;
     if (mx_all_small(T))
-        return launch_mx_grouped_class<64, MODE>(cls(3), total_rows / 64 + std::min<int64_t>(E, total_rows), st);
+        return launch_mx_grouped_class<64, MODE>(cls(kPlanSmall), total_rows / 64 + std::min<int64_t>(E, total_rows), st);
     if (total_rows > 128)
         s = launch_mx_grouped_class<256, MODE>(cls(0), total_rows / 128 + 1, st);
     if (s == NVFP4_OK && total_rows > 64)
         s = launch_mx_grouped_class<128, MODE>(cls(1), std::min<int64_t>(E, total_rows / 65 + 1), st);
     if (s == NVFP4_OK)
-        s = launch_mx_grouped_class<64, MODE>(cls(3), std::min<int64_t>(E, total_rows), st);
+        s = launch_mx_grouped_class<64, MODE>(cls(kPlanSmall), std::min<int64_t>(E, total_rows), st);
     return s;
 }
 
@@ -640,19 +717,24 @@ nvfp4_status mx_moe_check(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
 
 extern "C" {
 
-const char* nvfp4_status_string(nvfp4_status s)
+const char* nvfp4_status_string(int32_t s)
 {
     switch (s) {
-    case NVFP4_OK: return "ok";
-    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
-    case NVFP4_ERR_SHAPE: return "invalid shape";
-    case NVFP4_ERR_RANGE: return "value out of range";
-    case NVFP4_ERR_WORKSPACE: return "workspace too small";
-    case NVFP4_ERR_DEVICE: return "HIP device error";
-    case NVFP4_ERR_UNSUPPORTED: return "unsupported by this build";
+    case (int32_t)NVFP4_OK: return "ok";
+    case (int32_t)NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case (int32_t)NVFP4_ERR_SHAPE: return "invalid shape";
+    case (int32_t)NVFP4_ERR_RANGE: return "value out of range";
+    case (int32_t)NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case (int32_t)NVFP4_ERR_DEVICE: return "HIP device error";
+    case (int32_t)NVFP4_ERR_UNSUPPORTED: return "unsupported by this build";
+    case (int32_t)NVFP4_ERR_DATA: return "invalid data (non-finite input, bad block scale or global)";
     }
     return "unknown status";
 }
+
+const char* nvfp4_build_stamp(void) { return NVFP4_BUILD_STAMP; }
+
+int nvfp4_set_checks(int on) { return g_checks.exchange(on != 0 ? 1 : 0, std::memory_order_relaxed); }
 
 void nvfp4_recipe(int32_t out[6])
 {
@@ -709,7 +791,7 @@ nvfp4_status nvfp4_get_error(void* stream)
     return (nvfp4_status)v;
 }
 
-nvfp4_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+static nvfp4_status quantize_unchecked(const void* x, int64_t rows, int64_t cols, int64_t ld,
                             const float* static_global, const nvfp4_tensor* out, void* ws,
                             size_t ws_bytes, void* stream)
 {
@@ -734,7 +816,21 @@ nvfp4_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
     return quantize_impl(x, rows, cols, ld, kGlobalPartials, nullptr, out, 0, (uint32_t*)ws, S(stream));
 }
 
-nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dtype, void* stream)
+nvfp4_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                            const float* static_global, const nvfp4_tensor* out, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = quantize_unchecked(x, rows, cols, ld, static_global, out, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on()) {
+        check_bf16(x, rows, cols, ld, S(stream));
+        if (static_global)
+            check_globals(static_global, 1, S(stream));
+        s = launch_status();
+    }
+    return s;
+}
+
+static nvfp4_status dequantize_unchecked(const nvfp4_tensor* in, void* out, int32_t dtype, void* stream)
 {
     nvfp4_status s = check_tensor(in);
     if (s != NVFP4_OK)
@@ -757,8 +853,16 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, nvfp4_dtype dty
     return launch_status();
 }
 
-nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* ids, int64_t n, void* out,
-                                     nvfp4_dtype dtype, void* stream)
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, int32_t dtype, void* stream)
+{
+    nvfp4_status s = dequantize_unchecked(in, out, dtype, stream);
+    if (s == NVFP4_OK && checks_on())
+        s = check_tensor_data(in, S(stream));
+    return s;
+}
+
+static nvfp4_status gather_dequantize_unchecked(const nvfp4_tensor* table, const int32_t* ids, int64_t n, void* out,
+                                     int32_t dtype, void* stream)
 {
     nvfp4_status s = check_tensor(table);
     if (s != NVFP4_OK)
@@ -786,6 +890,15 @@ nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* i
             (const uint32_t*)table->packed, table->scales, table->global, ids, (uint32_t)n, table->rows,
             (uint32_t)hpr, out);
     return launch_status();
+}
+
+nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* ids, int64_t n, void* out,
+                                     int32_t dtype, void* stream)
+{
+    nvfp4_status s = gather_dequantize_unchecked(table, ids, n, out, dtype, stream);
+    if (s == NVFP4_OK && checks_on())
+        s = check_tensor_data(table, S(stream));
+    return s;
 }
 
 nvfp4_status mxfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* packed,
@@ -843,7 +956,7 @@ nvfp4_status mxfp4_to_nvfp4(const uint8_t* mx_packed, const uint8_t* e8m0, int64
     return launch_status();
 }
 
-nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, nvfp4_dtype dtype,
+static nvfp4_status gemm_unchecked(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, int32_t dtype,
                         void* ws, size_t ws_bytes, void* stream)
 {
     nvfp4_status s = check_tensor(A);
@@ -855,8 +968,6 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
         return NVFP4_ERR_INVALID_ARG;
     if (A->cols != W->cols || A->batch != 1 || W->batch != 1)
         return NVFP4_ERR_SHAPE;
-    if (A->cols % kBK != 0)
-        return NVFP4_ERR_UNSUPPORTED;
     if (A->rows == 0 || W->rows == 0)
         return NVFP4_OK;
     if (A->cols == 0)
@@ -888,8 +999,17 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, n
     return dispatch_dense(p, S(stream));
 }
 
-nvfp4_status nvfp4_gemm_w4a16(const void* a, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
-                              void* C, nvfp4_dtype dtype, void* ws, size_t ws_bytes, void* stream)
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, int32_t dtype,
+                        void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = gemm_unchecked(A, W, C, dtype, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on())
+        s = check_tensors_data({A, W}, S(stream));
+    return s;
+}
+
+static nvfp4_status gemm_w4a16_unchecked(const void* a, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
+                              void* C, int32_t dtype, void* ws, size_t ws_bytes, void* stream)
 {
     nvfp4_status s = check_tensor(W);
     if (s != NVFP4_OK)
@@ -930,6 +1050,17 @@ nvfp4_status nvfp4_gemm_w4a16(const void* a, int64_t M, int64_t K, int64_t lda, 
     return dispatch_dense(p, S(stream));
 }
 
+nvfp4_status nvfp4_gemm_w4a16(const void* a, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
+                              void* C, int32_t dtype, void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = gemm_w4a16_unchecked(a, M, K, lda, W, C, dtype, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on()) {
+        check_bf16(a, M, K, lda, S(stream));
+        s = check_tensors_data({W}, S(stream));
+    }
+    return s;
+}
+
 nvfp4_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* fp8, uint8_t* e8m0,
                             void* stream)
 {
@@ -946,7 +1077,7 @@ nvfp4_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
 }
 
 nvfp4_status mx_gemm_w4a8(const uint8_t* a, const uint8_t* a_e8m0, int64_t M, int64_t K, const uint8_t* w,
-                          const uint8_t* w_e8m0, int64_t N, void* C, nvfp4_dtype dtype, void* stream)
+                          const uint8_t* w_e8m0, int64_t N, void* C, int32_t dtype, void* stream)
 {
     if (M < 0 || N < 0 || K < 0)
         return NVFP4_ERR_SHAPE;
@@ -1139,8 +1270,8 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     }
     if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || xq->rows != T || xq->cols != H || xq->batch != 1)
         return NVFP4_ERR_SHAPE;
-    if (H % kBK != 0 || I % 128 != 0)
-        return NVFP4_ERR_UNSUPPORTED;
+    if (H % 16 != 0 || I % 16 != 0 || H == 0 || I == 0)
+        return NVFP4_ERR_SHAPE;
     const RouteLayout L = route_layout(T * k, E);
     if (ws_bytes < L.end)
         return NVFP4_ERR_WORKSPACE;
@@ -1169,18 +1300,29 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     p.M = T * k;
     p.ksplit = gpart ? ksplit : 1;
     p.partial = gpart;
-    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E, grouped_all_small(T, H, p.ksplit),
+    return dispatch_grouped<kModeGateUp>(p, offsets, T * k, E,
+                                         grouped_all_small(T, H, p.ksplit, grouped_ragged(kModeGateUp, H, I)),
                                          at<int32_t>(ws, L.plan_gu), plan_ready, st);
 }
 
-nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+static nvfp4_status moe_gate_up_unchecked(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
                                int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
                                uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream)
 {
     return moe_gate_up_impl(xq, perm, offsets, T, k, E, w13, h, h_amax, ws, ws_bytes, false, S(stream));
 }
 
-nvfp4_status nvfp4_moe_gate_up_q(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+nvfp4_status nvfp4_moe_gate_up(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+                               int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13, void* h,
+                               uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = moe_gate_up_unchecked(xq, perm, offsets, T, k, E, w13, h, h_amax, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on())
+        s = check_tensors_data({xq, w13}, S(stream));
+    return s;
+}
+
+static nvfp4_status moe_gate_up_q_unchecked(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
                                  int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13,
                                  const float* h_global, const nvfp4_tensor* hq, void* ws, size_t ws_bytes,
                                  void* stream)
@@ -1189,6 +1331,19 @@ nvfp4_status nvfp4_moe_gate_up_q(const nvfp4_tensor* xq, const int32_t* perm, co
         return NVFP4_ERR_INVALID_ARG;
     return moe_gate_up_impl(xq, perm, offsets, T, k, E, w13, nullptr, nullptr, ws, ws_bytes, false, S(stream),
                             1, nullptr, h_global, hq);
+}
+
+nvfp4_status nvfp4_moe_gate_up_q(const nvfp4_tensor* xq, const int32_t* perm, const int32_t* offsets,
+                                 int64_t T, int32_t k, int32_t E, const nvfp4_tensor* w13,
+                                 const float* h_global, const nvfp4_tensor* hq, void* ws, size_t ws_bytes,
+                                 void* stream)
+{
+    nvfp4_status s = moe_gate_up_q_unchecked(xq, perm, offsets, T, k, E, w13, h_global, hq, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on()) {
+        check_globals(h_global, 1, S(stream));
+        s = check_tensors_data({xq, w13}, S(stream));
+    }
+    return s;
 }
 
 static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
@@ -1205,8 +1360,8 @@ static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets
         return NVFP4_ERR_INVALID_ARG;
     if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || hq->rows != T * k || hq->cols != I || hq->batch != 1)
         return NVFP4_ERR_SHAPE;
-    if (I % kBK != 0 || H % 64 != 0)
-        return NVFP4_ERR_UNSUPPORTED;
+    if (H % 16 != 0 || I % 16 != 0 || H == 0 || I == 0)
+        return NVFP4_ERR_SHAPE;
     const RouteLayout L = route_layout(T * k, E);
     if (ws_bytes < L.end)
         return NVFP4_ERR_WORKSPACE;
@@ -1228,15 +1383,26 @@ static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets
     p.out = y;
     p.ksplit = ksplit;
     p.partial = y;
-    return dispatch_grouped<kModeDown>(p, offsets, T * k, E, grouped_all_small(T, I, ksplit),
+    return dispatch_grouped<kModeDown>(p, offsets, T * k, E,
+                                       grouped_all_small(T, I, ksplit, grouped_ragged(kModeDown, I, H)),
                                        at<int32_t>(ws, L.plan_dn), plan_ready, st);
+}
+
+static nvfp4_status moe_down_unchecked(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
+                            int32_t E, const nvfp4_tensor* w2, float* y, void* ws, size_t ws_bytes,
+                            void* stream)
+{
+    return moe_down_impl(hq, offsets, T, k, E, w2, y, 1, ws, ws_bytes, false, S(stream));
 }
 
 nvfp4_status nvfp4_moe_down(const nvfp4_tensor* hq, const int32_t* offsets, int64_t T, int32_t k,
                             int32_t E, const nvfp4_tensor* w2, float* y, void* ws, size_t ws_bytes,
                             void* stream)
 {
-    return moe_down_impl(hq, offsets, T, k, E, w2, y, 1, ws, ws_bytes, false, S(stream));
+    nvfp4_status s = moe_down_unchecked(hq, offsets, T, k, E, w2, y, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on())
+        s = check_tensors_data({hq, w2}, S(stream));
+    return s;
 }
 
 nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* w, int64_t T, int32_t k,
@@ -1253,10 +1419,10 @@ nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* 
     return launch_status();
 }
 
-nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const float* w, int64_t T,
-                                    int32_t k, int32_t E, const nvfp4_tensor* w13,
-                                    const nvfp4_tensor* w2, const float* static_in_globals, void* out,
-                                    void* ws, size_t ws_bytes, void* stream)
+static nvfp4_status moe_grouped_gemm_impl(const void* x, const int32_t* ids, const float* w, int64_t T,
+                                          int32_t k, int32_t E, const nvfp4_tensor* w13,
+                                          const nvfp4_tensor* w2, const float* static_in_globals, void* out,
+                                          void* ws, size_t ws_bytes, void* stream)
 {
     int64_t H = 0, I = 0;
     nvfp4_status s = check_experts(w13, w2, E, &H, &I);
@@ -1264,8 +1430,8 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
         return s;
     if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    if (H % kBK != 0 || I % 128 != 0)
-        return NVFP4_ERR_UNSUPPORTED;
+    if (H % 16 != 0 || I % 16 != 0 || H == 0 || I == 0)
+        return NVFP4_ERR_SHAPE;
     if (T == 0)
         return NVFP4_OK;
     if (!x || !ids || !w || !out || !ws || !aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256))
@@ -1283,11 +1449,12 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     const int ksplit = moe_down_ksplit(T, k, E, H, I);
     const int gsplit = moe_gate_ksplit(T, k, E, H, I);
     const bool small = T * k <= kRouteSmall;
+    const bool rag_gu = grouped_ragged(kModeGateUp, H, I), rag_dn = grouped_ragged(kModeDown, I, H);
+    const int small_gu = grouped_all_small(T, H, gsplit, rag_gu), small_dn = grouped_all_small(T, I, ksplit, rag_dn);
     if (small)
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
-                       grouped_small_bm(H, grouped_all_small(T, H, gsplit), T * k, E), grouped_all_small(T, H, gsplit),
-                       at<int32_t>(ws, L.r.plan_dn), grouped_small_bm(I, grouped_all_small(T, I, ksplit), T * k, E),
-                       grouped_all_small(T, I, ksplit));
+                       grouped_small_bm(H, small_gu, T * k, E, rag_gu), small_gu, at<int32_t>(ws, L.r.plan_dn),
+                       grouped_small_bm(I, small_dn, T * k, E, rag_dn), small_dn);
     else
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
     if (s != NVFP4_OK)
@@ -1330,7 +1497,23 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const flo
     return launch_status();
 }
 
-nvfp4_status nvfp4_moe_w4a16(const void* x, const int32_t* ids, const float* w, int64_t T, int32_t k,
+nvfp4_status nvfp4_moe_grouped_gemm(const void* x, const int32_t* ids, const float* w, int64_t T,
+                                    int32_t k, int32_t E, const nvfp4_tensor* w13,
+                                    const nvfp4_tensor* w2, const float* static_in_globals, void* out,
+                                    void* ws, size_t ws_bytes, void* stream)
+{
+    nvfp4_status s =
+        moe_grouped_gemm_impl(x, ids, w, T, k, E, w13, w2, static_in_globals, out, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on() && T > 0) {
+        check_bf16(x, T, w13->cols, w13->cols, S(stream));
+        if (static_in_globals)
+            check_globals(static_in_globals, 2, S(stream));
+        s = check_tensors_data({w13, w2}, S(stream));
+    }
+    return s;
+}
+
+static nvfp4_status moe_w4a16_unchecked(const void* x, const int32_t* ids, const float* w, int64_t T, int32_t k,
                              int32_t E, const nvfp4_tensor* w13, const nvfp4_tensor* w2, void* out, void* ws,
                              size_t ws_bytes, void* stream)
 {
@@ -1413,6 +1596,18 @@ nvfp4_status nvfp4_moe_w4a16(const void* x, const int32_t* ids, const float* w, 
     return launch_status();
 }
 
+nvfp4_status nvfp4_moe_w4a16(const void* x, const int32_t* ids, const float* w, int64_t T, int32_t k,
+                             int32_t E, const nvfp4_tensor* w13, const nvfp4_tensor* w2, void* out, void* ws,
+                             size_t ws_bytes, void* stream)
+{
+    nvfp4_status s = moe_w4a16_unchecked(x, ids, w, T, k, E, w13, w2, out, ws, ws_bytes, stream);
+    if (s == NVFP4_OK && checks_on() && T > 0) {
+        check_bf16(x, T, w13->cols, w13->cols, S(stream));
+        s = check_tensors_data({w13, w2}, S(stream));
+    }
+    return s;
+}
+
 nvfp4_status nvfp4_kv_quant(const void* k, const void* v, int64_t n, int64_t heads, int64_t tok_offset,
                             const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache, void* stream)
 {
@@ -1453,8 +1648,8 @@ nvfp4_status nvfp4_kv_quant(const void* k, const void* v, int64_t n, int64_t hea
     return launch_quantize(a, nt, S(stream));
 }
 
-nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache, int64_t heads,
-                              int64_t tok_begin, int64_t n, void* k_out, void* v_out, nvfp4_dtype dtype,
+static nvfp4_status kv_dequant_unchecked(const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache, int64_t heads,
+                              int64_t tok_begin, int64_t n, void* k_out, void* v_out, int32_t dtype,
                               void* stream)
 {
     const nvfp4_tensor* src[2] = {k_cache, v_cache};
@@ -1493,6 +1688,16 @@ nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v
             return s;
     }
     return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v_cache, int64_t heads,
+                              int64_t tok_begin, int64_t n, void* k_out, void* v_out, int32_t dtype,
+                              void* stream)
+{
+    nvfp4_status s = kv_dequant_unchecked(k_cache, v_cache, heads, tok_begin, n, k_out, v_out, dtype, stream);
+    if (s == NVFP4_OK && checks_on())
+        s = check_tensors_data({k_out ? k_cache : nullptr, v_out ? v_cache : nullptr}, S(stream));
+    return s;
 }
 
 nvfp4_status nvfp4_audit_scales(const nvfp4_tensor* t, int64_t* counts, void* stream)

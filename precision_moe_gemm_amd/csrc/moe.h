@@ -181,13 +181,13 @@ tile_offsets_kernel(const int32_t* __restrict__ offsets, int E, int bm, int32_t*
 // spent on padding rows when the tokens per expert are skewed:
 //   class 0: 256-row tiles (the full tiles, and remainders r > 128)
 //   class 1: 128-row tiles (64 < r <= 128)
-//   class 2: unused (kept so that class indices match the tile shapes)
-//   class 3: `small_bm`-row tiles (r <= 64; small_bm is 16 or 32)
-// With `all_small`, every expert's rows go to class 3 instead.
+//   class 2: `small_bm`-row tiles (r <= 64; small_bm is 16, 32 or 64)
+// With `all_small`, every expert's rows go to class 2 instead.
 // For class c, plan + 3 c (E + 1) holds tile_off[E + 1] (exclusive prefix of
 // the class's tiles per expert), then row_base[E + 1] and row_lim[E + 1]:
 // tile i of expert e covers rows [row_base[e] + i bm, min(+bm, row_lim[e])).
-constexpr int kPlanClasses = 4;
+constexpr int kPlanClasses = 3;
+constexpr int kPlanSmall = 2;  // the small-tile class
 
 // Class C's share of expert rows [lo, hi): its tile count, row base and row
 // limit (scalars, so the callers' unrolled class loops stay in registers).
@@ -198,18 +198,18 @@ template <int C>
 NVFP4_DEV ClassPlan plan_class(int32_t lo, int32_t hi, int small_bm, int all_small)
 {
     if (all_small) {
-        // every row in class-3 tiles (K-split streaming projections)
-        if (C == 3)
+        // every row in small tiles (K-split streaming projections)
+        if (C == kPlanSmall)
             return ClassPlan{(hi - lo + small_bm - 1) / small_bm, lo, hi};
         return ClassPlan{0, lo, lo};
     }
     const int32_t rows = hi - lo, nf = rows >> 8, r = rows & 255;
     const int32_t tail = lo + (nf << 8);
-    const int c = r > 128 ? 0 : r > 64 ? 1 : 3;
+    const int c = r > 128 ? 0 : r > 64 ? 1 : kPlanSmall;
     if (C == 0)
         return ClassPlan{nf + (c == 0 && r > 0 ? 1 : 0), lo, c == 0 ? hi : tail};
-    if (C == 3)
-        return ClassPlan{c == 3 ? (r + small_bm - 1) / small_bm : 0, tail, c == 3 ? hi : tail};
+    if (C == kPlanSmall)
+        return ClassPlan{c == kPlanSmall ? (r + small_bm - 1) / small_bm : 0, tail, c == kPlanSmall ? hi : tail};
     return ClassPlan{c == C ? 1 : 0, tail, c == C ? hi : tail};
 }
 
@@ -220,22 +220,20 @@ NVFP4_DEV void plan_block(const int32_t* offs, int E, int small_bm, int all_smal
 {
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
-    int32_t cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
+    int32_t cnt0 = 0, cnt1 = 0, cnt2 = 0;
     for (int e = e0; e < e0 + per && e < E; e++) {
         const int32_t lo = offs[e], hi = offs[e + 1];
         cnt0 += plan_class<0>(lo, hi, small_bm, all_small).tiles;
         cnt1 += plan_class<1>(lo, hi, small_bm, all_small).tiles;
         cnt2 += plan_class<2>(lo, hi, small_bm, all_small).tiles;
-        cnt3 += plan_class<3>(lo, hi, small_bm, all_small).tiles;
     }
     // when every row takes small tiles the other classes are empty: their
     // counts are zero in every thread, so their scans are skipped
     const ScanResult zero{0, 0};
     const ScanResult s0 = all_small ? zero : block_exclusive_scan(cnt0, lds16);
     const ScanResult s1 = all_small ? zero : block_exclusive_scan(cnt1, lds16);
-    const ScanResult s2 = all_small ? zero : block_exclusive_scan(cnt2, lds16);
-    const ScanResult s3 = block_exclusive_scan(cnt3, lds16);
-    int32_t run0 = s0.prefix, run1 = s1.prefix, run2 = s2.prefix, run3 = s3.prefix;
+    const ScanResult s2 = block_exclusive_scan(cnt2, lds16);
+    int32_t run0 = s0.prefix, run1 = s1.prefix, run2 = s2.prefix;
     auto put = [&](int c, int e, const ClassPlan& cp, int32_t& run) {
         int32_t* pc = plan + 3 * c * (E + 1);
         pc[e] = run;
@@ -248,13 +246,11 @@ NVFP4_DEV void plan_block(const int32_t* offs, int E, int small_bm, int all_smal
         put(0, e, plan_class<0>(lo, hi, small_bm, all_small), run0);
         put(1, e, plan_class<1>(lo, hi, small_bm, all_small), run1);
         put(2, e, plan_class<2>(lo, hi, small_bm, all_small), run2);
-        put(3, e, plan_class<3>(lo, hi, small_bm, all_small), run3);
     }
     if (threadIdx.x == 0) {
         plan[E] = s0.total;
         plan[3 * (E + 1) + E] = s1.total;
         plan[6 * (E + 1) + E] = s2.total;
-        plan[9 * (E + 1) + E] = s3.total;
     }
 }
 

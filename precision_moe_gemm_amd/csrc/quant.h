@@ -289,6 +289,46 @@ audit_kernel(const uint8_t* __restrict__ scales, int64_t n, unsigned long long* 
         atomicAdd(&counts[0], (unsigned long long)n);
 }
 
+// ---- optional data checks (nvfp4_set_checks): raise NVFP4_ERR_DATA ---------
+// E4M3 scale bytes: a NaN pattern (0x7F, 0xFF) or a set sign bit.
+__global__ void __launch_bounds__(kQuantThreads)
+check_scales_kernel(const uint8_t* __restrict__ s, int64_t n)
+{
+    bool bad = false;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint8_t b = s[i];
+        bad |= (b & 0x80) != 0 || (b & 0x7F) == 0x7F;
+    }
+    if (bad)
+        raise_error(NVFP4_ERR_DATA);
+}
+
+// fp32 globals: each finite and positive.
+__global__ void check_globals_kernel(const float* __restrict__ g, int64_t n)
+{
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const float v = g[i];
+        if (!(v > 0.0f) || __builtin_isinf(v))
+            raise_error(NVFP4_ERR_DATA);
+    }
+}
+
+// bf16 rows [rows, cols] with row stride ld: every value finite.
+__global__ void __launch_bounds__(kQuantThreads)
+check_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld)
+{
+    bool bad = false;
+    const int64_t total = rows * cols;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / cols, c = i - r * cols;
+        bad |= (x[r * ld + c] & 0x7F80u) == 0x7F80u;
+    }
+    if (bad)
+        raise_error(NVFP4_ERR_DATA);
+}
+
 __global__ void zero_u64_kernel(unsigned long long* p, int n)
 {
     if ((int)threadIdx.x < n)

@@ -51,6 +51,19 @@ def rel_err(got, ref):
     return float(np.abs(got - ref).max() / den)
 
 
+def elem_rel_err(got, ref, floor=1e-2):
+    """Element-wise companion of rel_err: max |got - ref| / |ref| over the
+    elements with |ref| >= floor * max |ref| (the floor keeps outputs that
+    cancel to near zero, where fp32 summation order dominates, out of it)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.abs(ref).max()
+    if den == 0:
+        return float(np.abs(got).max())
+    sel = np.abs(ref) >= floor * den
+    return float((np.abs(got[sel] - ref[sel]) / np.abs(ref[sel])).max())
+
+
 def bf16_to_f64(b):
     return (np.asarray(b).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
@@ -60,4 +73,7 @@ def tensor_bf16_to_f64(t):
 
 
 BF16_HALF_ULP = 2.0 ** -8
+# one bf16 ulp relative to the value (7 stored mantissa bits): the element-wise
+# bound of a bf16 output whose fp32 source is within the GEMM tolerance
+BF16_ULP = 2.0 ** -7
 GEMM_TOL = 1e-3

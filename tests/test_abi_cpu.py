@@ -10,7 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
-LIB = os.path.join(ROOT, "precision_moe_gemm_amd", "libnvfp4.so")
+LIB = os.environ.get("NVFP4_LIB_PATH") or os.path.join(ROOT, "precision_moe_gemm_amd", "libnvfp4.so")
 
 
 def _declared():
@@ -86,10 +86,9 @@ def test_host_validation_fails_before_launch(lib):
     # bad dtype
     T4 = _lib.NVFP4TensorC(16, 16, 16, 4, 32, 1)
     assert lib.nvfp4_dequantize(ctypes.byref(T4), ctypes.c_void_p(16), 7, None) == _lib.INVALID_ARG
-    # GEMM with K not a multiple of 64 -> unsupported; mismatched K -> shape
+    # GEMM: K any multiple of 16 (80 passes validation; mismatched K -> shape)
     A = _lib.NVFP4TensorC(16, 16, 16, 4, 80, 1)
     W = _lib.NVFP4TensorC(16, 16, 16, 8, 80, 1)
-    assert lib.nvfp4_gemm(ctypes.byref(A), ctypes.byref(W), ctypes.c_void_p(16), 0, None, 0, None) == _lib.UNSUPPORTED
     # a workspace smaller than the split needs -> workspace error
     A1 = _lib.NVFP4TensorC(16, 16, 16, 1, 4096, 1)
     W1 = _lib.NVFP4TensorC(16, 16, 16, 256, 4096, 1)
@@ -112,6 +111,12 @@ def test_host_validation_fails_before_launch(lib):
     assert lib.nvfp4_moe_grouped_gemm(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 8, 2,
                                       4, ctypes.byref(w13), ctypes.byref(w2), None, ctypes.c_void_p(16),
                                       ctypes.c_void_p(256), 64, None) == _lib.WORKSPACE
+    # MoE: hidden size not a multiple of 16 -> shape (I = 40 is one: tensor cols)
+    w13 = _lib.NVFP4TensorC(16, 16, 16, 80, 40, 4)
+    w2 = _lib.NVFP4TensorC(16, 16, 16, 40, 40, 4)
+    assert lib.nvfp4_moe_grouped_gemm(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 8, 2,
+                                      4, ctypes.byref(w13), ctypes.byref(w2), None, ctypes.c_void_p(16),
+                                      ctypes.c_void_p(256), 1 << 30, None) == _lib.SHAPE
     # KV write past the cache end -> shape
     kc = _lib.NVFP4TensorC(16, 16, 16, 64, 256, 1)
     assert lib.nvfp4_kv_quant(ctypes.c_void_p(16), None, 9, 4, 8, ctypes.byref(kc), ctypes.byref(kc),
@@ -124,3 +129,23 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_stale_library_is_refused(lib, monkeypatch):
+    """The loader compares the library's build stamp (a hash of the sources
+    and flags it was built from) with the source tree."""
+    from precision_moe_gemm_amd import _lib, build
+    assert lib.nvfp4_build_stamp().decode() == build.source_hash()
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0123456789abcdef")
+    with pytest.raises(ImportError, match="other sources"):
+        _lib.load()
+
+
+def test_check_switch_is_host_state(lib):
+    """nvfp4_set_checks returns the previous setting (host only, no launch)."""
+    prev = lib.nvfp4_set_checks(1)
+    assert lib.nvfp4_set_checks(0) == 1
+    assert lib.nvfp4_set_checks(prev) == 0
+    import precision_moe_gemm_amd as nv
+    assert "invalid data" in nv.status_string(7)

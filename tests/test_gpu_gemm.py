@@ -11,7 +11,7 @@ import torch
 import oracle
 import precision_moe_gemm_amd as nv
 from precision_moe_gemm_amd import synth
-from tests.gpu_util import BF16_HALF_ULP, GEMM_TOL, assert_same_nvfp4, rel_err, step, to_oracle, u8
+from tests.gpu_util import BF16_HALF_ULP, GEMM_TOL, assert_same_nvfp4, elem_rel_err, rel_err, step, to_oracle, u8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -155,12 +155,13 @@ def test_dense_mlp_gate_up_sampled(orc, M):
     del w, W, C
 
 
-def test_unsupported_k():
-    A = nv.NVFP4Tensor.empty(4, 80, 1, DEV)
-    W = nv.NVFP4Tensor.empty(8, 80, 1, DEV)
+def test_k_not_multiple_of_16_is_a_shape_error():
+    """The format blocks K by 16: other K are refused before any launch."""
+    A = nv.NVFP4Tensor.empty(4, 72, 1, DEV)
+    W = nv.NVFP4Tensor.empty(8, 72, 1, DEV)
     with pytest.raises(nv.NVFP4Error) as ei:
         nv.nvfp4_gemm(A, W)
-    assert ei.value.status == 6
+    assert ei.value.status == 2
 
 
 def test_gemm_deterministic():
@@ -192,3 +193,33 @@ def test_pow2_weight_scales(orc, M, N, K):
     err = rel_err(C.cpu().numpy(), orc.gemm(Ao, Wo))
     print(f"pow2 scales rel err {err:.3e}")
     assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M", [40, 100, 300])
+def test_down_projection_K17408(orc, M):
+    """The 27B-class down projection (W 5120 x 17408; page "Qwen3.8-27B-NVFP4",
+    section 2) at M = 40 (64-row register-decode tiles), 100 (a 128-row tile)
+    and 300 (a 256-row tile and a partial one): every row of A against 256
+    sampled columns, W's sampled rows bit-exact vs the oracle."""
+    N, K = 5120, 17408
+    x = synth.normal_bf16((M, K), 1.0, (320, M), DEV)
+    w = synth.normal_bf16((N, K), 0.02, (321, N), DEV)
+    step(f"gemm down projection M={M} N={N} K={K}")
+    A, W = nv.nvfp4_quantize(x), nv.nvfp4_quantize(w)
+    C = nv.nvfp4_gemm(A, W)
+    torch.cuda.synchronize()
+    Ao = orc.quantize(synth.bits(x))
+    assert_same_nvfp4(A, Ao)
+    cols = np.unique(np.r_[np.random.default_rng(M).choice(N, 254, replace=False), 0, N - 1])
+    wb = synth.bits(w)
+    Gw = orc.global_from_amax(orc.amax_bf16(wb))
+    Wo = orc.quantize(np.ascontiguousarray(wb[cols]), static_G=Gw)
+    assert np.float32(W.global_.item()) == np.float32(Gw)
+    np.testing.assert_array_equal(u8(W.scales)[0][cols], Wo.scales)
+    np.testing.assert_array_equal(u8(W.packed)[0][cols], Wo.packed)
+    R = orc.gemm(Ao, Wo)
+    got = C.cpu().numpy()[:, cols]
+    err, eerr = rel_err(got, R), elem_rel_err(got, R)
+    print(f"down projection M={M} rel err {err:.3e} (element-wise {eerr:.3e})")
+    assert err <= GEMM_TOL
+    assert eerr <= GEMM_TOL

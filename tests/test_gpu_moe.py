@@ -174,16 +174,6 @@ def test_moe_many_items_per_workgroup(orc):
     _check_moe(orc, cfg)
 
 
-def test_moe_512_experts_top10_sampled(orc):
-    """512 experts, top-10, T=4096, H=4096, I=1024 at full size."""
-    _check_moe(orc, synth.C3, sample_rows=24, sample_tokens=6)
-
-
-def test_moe_384_experts_decode_sampled(orc):
-    """384 MXFP4-origin experts, top-8, H=7168, I=2048, T=64 (decode batch)."""
-    _check_moe(orc, synth.C4_DECODE, sample_rows=24, sample_tokens=6)
-
-
 def test_fused_down_k_split_small(orc):
     """A batch of 12 tokens over 2 experts with I = 2048: the fused layer splits
     the down projection's K over two streaming workgroups."""

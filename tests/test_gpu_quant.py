@@ -199,3 +199,19 @@ def test_gather_dequantize_bad_ids_and_empty(orc):
     np.testing.assert_array_equal(f.view(np.uint32), orc.gather_dequantize(ref, ids).view(np.uint32))
     e = nv.nvfp4_gather_dequantize(t, torch.zeros(0, dtype=torch.int32, device=DEV))
     assert e.shape == (0, 128)
+
+
+def test_audit_counts_planted_bytes(orc):
+    """NaN-pattern, zero, negative-zero, negative and 448 scale bytes planted
+    in a tensor: the device audit gives the hand counts and the oracle's."""
+    from tests.test_oracle_quant import AUDIT_EXPECT, audit_planted_scales
+    s = audit_planted_scales()
+    t = nv.NVFP4Tensor(torch.zeros((1, 3, 96), dtype=torch.uint8, device=DEV),
+                       torch.from_numpy(s).reshape(1, 3, 12).to(DEV),
+                       torch.ones(1, dtype=torch.float32, device=DEV), 3, 192, 1)
+    step("audit planted scale bytes")
+    counts = nv.nvfp4_audit_scales(t).cpu().numpy().tolist()
+    want = [AUDIT_EXPECT[k] for k in ("total", "nonfinite", "nonpositive", "at_max")]
+    assert counts == want
+    a = orc.audit_scales(orc.NVFP4(np.zeros((3, 96), np.uint8), s, 1.0))
+    assert counts == [a["total"], a["nonfinite"], a["nonpositive"], a["at_max"]]

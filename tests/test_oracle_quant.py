@@ -278,3 +278,27 @@ def test_gather_dequantize_selects_rows(orc):
     f, b = orc.gather_dequantize(t, ids, want_bf16=True)
     assert np.array_equal(f, g)
     assert np.array_equal(b, orc.dequantize(t, want_bf16=True)[1][ids])
+
+
+# Planted scale bytes for the audit (page "Qwen3.8-Flash-Next-NVFP4", section
+# 证据链: every scale must be finite and positive).  E4M3FN has one NaN
+# pattern per sign (0x7F, 0xFF) and no infinities; zero is 0x00 or 0x80 and
+# a set sign bit makes a scale negative.  Counts written out by hand:
+AUDIT_PLANT = {0x7F: 3, 0xFF: 2, 0x00: 4, 0x80: 5, 0xB8: 6, 0x7E: 7, 0x38: 9}
+AUDIT_EXPECT = dict(total=36, nonfinite=3 + 2, nonpositive=2 + 4 + 5 + 6, at_max=7)
+
+
+def audit_planted_scales():
+    """A [3, 12]-byte scale array (36 blocks) holding the planted bytes in a
+    fixed shuffled order; the codes are irrelevant to the audit."""
+    vals = [b for b, n in AUDIT_PLANT.items() for _ in range(n)]
+    assert len(vals) == 36
+    order = np.random.default_rng(4).permutation(36)
+    return np.asarray(vals, np.uint8)[order].reshape(3, 12)
+
+
+def test_audit_counts_planted_bytes(orc):
+    s = audit_planted_scales()
+    t = orc.NVFP4(np.zeros((3, 96), np.uint8), s, 1.0)
+    a = orc.audit_scales(t)
+    assert a == AUDIT_EXPECT
