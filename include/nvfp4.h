@@ -339,6 +339,29 @@ nvfp4_status nvfp4_moe_grouped_gemm(const void* x_bf16, const int32_t* topk_ids,
                                     const float* static_in_globals, void* out_bf16,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * nvfp4_moe_grouped_gemm without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus ws), same
+ * kernels and bit-identical output; the workspace is a library-owned device
+ * array of nvfp4_noalloc_scratch_bytes() bytes (32 MiB) per GPU, held from
+ * the library's first use on that GPU until the process ends.  A layer whose
+ * workspace (nvfp4_workspace_size(NVFP4_OP_MOE, ...)) exceeds it gives
+ * NVFP4_ERR_WORKSPACE before any launch (decode-sized batches fit: the
+ * 384-expert T = 64 layer needs 18 MB).  No call allocates or frees.  Every
+ * call on a GPU shares that GPU's array, which keeps the previous call's
+ * contents (nothing in it needs to start at zero): calls that overlap in
+ * time on one GPU -- on different streams or from different host threads --
+ * race and give undefined results.
+ */
+nvfp4_status nvfp4_moe_grouped_gemm_noalloc(const void* x_bf16, const int32_t* topk_ids,
+                                            const float* topk_w, int64_t T, int32_t k, int32_t E,
+                                            const nvfp4_tensor* w13, const nvfp4_tensor* w2,
+                                            const float* static_in_globals, void* out_bf16, void* stream);
+
+/* Host: bytes of the per-GPU scratch array of nvfp4_moe_grouped_gemm_noalloc. */
+size_t nvfp4_noalloc_scratch_bytes(void);
+
 /* ---- staged MoE entry points (the steps of nvfp4_moe_grouped_gemm) ---- */
 
 /*

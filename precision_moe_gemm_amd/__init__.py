@@ -20,7 +20,7 @@ from . import _lib
 
 __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
-    "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm",
+    "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm", "nvfp4_moe_grouped_gemm_noalloc",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
     "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8", "mx_moe_w4a8", "mx_moe_gate_up", "mx_moe_down",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error", "nvfp4_set_checks",
@@ -299,6 +299,23 @@ def nvfp4_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torc
         _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, E, ctypes.byref(c13), ctypes.byref(c2),
         _ptr(static_in_globals), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
         "nvfp4_moe_grouped_gemm")
+    return out
+
+
+def nvfp4_moe_grouped_gemm_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                                   w13: NVFP4Tensor, w2: NVFP4Tensor, static_in_globals: torch.Tensor | None = None,
+                                   out: torch.Tensor | None = None):
+    """nvfp4_moe_grouped_gemm on the library's own device scratch (no
+    workspace; for callers that cannot allocate, pass `out`)."""
+    _need_cuda(x, topk_ids, topk_w)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    c13, c2 = w13.c(), w2.c()
+    _check(_lib.load().nvfp4_moe_grouped_gemm_noalloc(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, w13.batch, ctypes.byref(c13), ctypes.byref(c2),
+        _ptr(static_in_globals), _ptr(out), _stream(x.device)), "nvfp4_moe_grouped_gemm_noalloc")
     return out
 
 

@@ -61,6 +61,8 @@ SIGNATURES = {
                             P]),
     "mx_moe_down": (ST, [P, P, P, I64, ctypes.c_int32, ctypes.c_int32, I64, I64, P, P, P, P, ctypes.c_size_t, P]),
     "nvfp4_moe_w4a16": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, SZ, P]),
+    "nvfp4_moe_grouped_gemm_noalloc": (ST, [P, P, P, I64, I32, I32, TP, TP, P, P, P]),
+    "nvfp4_noalloc_scratch_bytes": (SZ, []),
     "nvfp4_moe_route": (ST, [P, I64, I32, I32, P, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up": (ST, [TP, P, P, I64, I32, I32, TP, P, P, P, SZ, P]),
     "nvfp4_moe_gate_up_q": (ST, [TP, P, P, I64, I32, I32, TP, P, TP, P, SZ, P]),

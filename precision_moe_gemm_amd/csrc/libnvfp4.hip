@@ -715,6 +715,44 @@ nvfp4_status mx_moe_check(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
     return NVFP4_OK;
 }
 
+// ---------------------------------------------------------------- scratch
+// Library-owned device scratch for the allocation-free MoE entry point
+// (nvfp4_moe_grouped_gemm_noalloc): one array per GPU, held from the first
+// use of the library on that GPU until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// for the device symbol): it takes the device address from
+// hipGetSymbolAddress once per device, with that device current, and uses
+// only that address.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or null with the
+// failing status in *st.
+void* scratch_address(nvfp4_status* st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *st = NVFP4_ERR_DEVICE;
+        return nullptr;
+    }
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr)
+        return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        *st = NVFP4_ERR_DEVICE;
+        return nullptr;
+    }
+    // threads racing on the first call obtain the same address
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+}  // namespace
+
 extern "C" {
 
 const char* nvfp4_status_string(int32_t s)
@@ -1594,6 +1632,39 @@ static nvfp4_status moe_w4a16_unchecked(const void* x, const int32_t* ids, const
     combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
                                                                    (u32x2*)out);
     return launch_status();
+}
+
+size_t nvfp4_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+nvfp4_status nvfp4_moe_grouped_gemm_noalloc(const void* x, const int32_t* ids, const float* w, int64_t T,
+                                            int32_t k, int32_t E, const nvfp4_tensor* w13,
+                                            const nvfp4_tensor* w2, const float* static_in_globals,
+                                            void* out, void* stream)
+{
+    int64_t H = 0, I = 0;
+    nvfp4_status s = check_experts(w13, w2, E, &H, &I);
+    if (s != NVFP4_OK)
+        return s;
+    if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * k > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    if (H % 16 != 0 || I % 16 != 0 || H == 0 || I == 0)
+        return NVFP4_ERR_SHAPE;
+    if (T == 0)
+        return NVFP4_OK;
+    // the workspace of this layer must fit the scratch array
+    if (moe_layout(T, k, E, H, I).end > kScratchBytes)
+        return NVFP4_ERR_WORKSPACE;
+    void* ws = scratch_address(&s);
+    if (!ws)
+        return s;
+    s = moe_grouped_gemm_impl(x, ids, w, T, k, E, w13, w2, static_in_globals, out, ws, kScratchBytes, stream);
+    if (s == NVFP4_OK && checks_on()) {
+        check_bf16(x, T, H, H, S(stream));
+        if (static_in_globals)
+            check_globals(static_in_globals, 2, S(stream));
+        s = check_tensors_data({w13, w2}, S(stream));
+    }
+    return s;
 }
 
 nvfp4_status nvfp4_moe_w4a16(const void* x, const int32_t* ids, const float* w, int64_t T, int32_t k,
