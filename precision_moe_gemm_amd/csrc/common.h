@@ -26,6 +26,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // an error with atomicCAS so the first one wins.
 __device__ unsigned int g_nvfp4_error;
 
+// Load from a table that no kernel in flight writes (produced by an earlier
+// launch, or an input): through the constant address space, so that a
+// uniform index becomes a scalar load, counted apart from the vector loads
+// in flight.
+template <class T>
+NVFP4_DEV T const_load(const T* ptr, int64_t i)
+{
+    typedef const __attribute__((address_space(4))) T* cptr;
+    return ((cptr)(uintptr_t)ptr)[i];
+}
+
 NVFP4_DEV void raise_error(unsigned code)
 {
     atomicCAS(&g_nvfp4_error, 0u, code);

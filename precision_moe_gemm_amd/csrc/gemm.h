@@ -160,16 +160,6 @@ NVFP4_DEV int64_t xcd_item(int64_t items)
     return (j < per && it < items) ? it : -1;
 }
 
-// Load from a table that no kernel in flight writes (produced by an earlier
-// launch): through the constant address space, so that a uniform index
-// becomes a scalar load, counted apart from the vector loads in flight.
-template <class T>
-NVFP4_DEV T const_load(const T* ptr, int64_t i)
-{
-    typedef const __attribute__((address_space(4))) T* cptr;
-    return ((cptr)(uintptr_t)ptr)[i];
-}
-
 template <int V>
 struct IntC {
     static constexpr int value = V;

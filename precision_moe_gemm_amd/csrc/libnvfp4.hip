@@ -45,6 +45,21 @@ inline unsigned stream_grid(int64_t work, int64_t cap = 8192)
     return (unsigned)std::min<int64_t>(g, cap);
 }
 
+// Router-weighted combine of `planes` planes of y into bf16 out [T, H]: one
+// workgroup per token and column slice; small batches split the columns so
+// that about 2048 workgroups run.
+void launch_combine(const float* y, const int32_t* inv, const float* w, int64_t T, int k, int64_t H, int planes,
+                    int64_t plane, void* out, hipStream_t st)
+{
+    const int64_t groups = H / 4;
+    if (T <= 0 || groups <= 0)
+        return;
+    int64_t split = std::max<int64_t>(1, std::min<int64_t>(ceil_div(2048, T), ceil_div(groups, 64)));
+    const unsigned gx = (unsigned)std::min<int64_t>(T, 65535);
+    combine_kernel<<<dim3(gx, (unsigned)split), 256, 0, st>>>(y, inv, w, T, k, H, planes, plane, (int)split,
+                                                              (u32x2*)out);
+}
+
 // An empty tensor (rows or cols 0) may carry null code/scale pointers.
 nvfp4_status check_tensor(const nvfp4_tensor* t, bool need_global = true)
 {
@@ -1109,8 +1124,9 @@ nvfp4_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
         return NVFP4_OK;
     if (!x || !fp8 || !e8m0 || !aligned(x, 16) || !aligned(fp8, 16))
         return NVFP4_ERR_INVALID_ARG;
-    mxfp8_encode_kernel<<<stream_grid(nblk, 8192), kMx8Threads, 0, S(stream)>>>(
-        (const u32x4*)x, rows, cols / 32, ld / 8, (u32x4*)fp8, e8m0);
+    // 4 chunks of 8 elements per thread per trip
+    mxfp8_encode_kernel<4><<<stream_grid(ceil_div(4 * nblk, 4), 8192), kMx8Threads, 0, S(stream)>>>(
+        (const u32x4*)x, rows, cols / 32, ld / 8, (u32x2*)fp8, e8m0);
     return launch_status();
 }
 
@@ -1240,8 +1256,7 @@ nvfp4_status mx_moe_w4a8(const void* x, const int32_t* ids, const float* w, int6
                               at<float>(ws, L.y), plan, true, st)) != NVFP4_OK)
         return s;
     // 6. router-weighted combine
-    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(at<float>(ws, L.y), inv, w, T, k, H, 1, 0,
-                                                                   (u32x2*)out);
+    launch_combine(at<float>(ws, L.y), inv, w, T, k, H, 1, 0, out, st);
     return launch_status();
 }
 
@@ -1452,8 +1467,7 @@ nvfp4_status nvfp4_moe_combine(const float* y, const int32_t* inv, const float* 
         return NVFP4_OK;
     if (!y || !inv || !w || !out || !aligned(y, 16) || !aligned(out, 8))
         return NVFP4_ERR_INVALID_ARG;
-    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, S(stream)>>>(y, inv, w, T, k, H, 1, 0,
-                                                                           (u32x2*)out);
+    launch_combine(y, inv, w, T, k, H, 1, 0, out, S(stream));
     return launch_status();
 }
 
@@ -1530,8 +1544,7 @@ static nvfp4_status moe_grouped_gemm_impl(const void* x, const int32_t* ids, con
     // 6. combine (adds the planes of y in order)
     if (!w || H % 8 != 0)
         return NVFP4_ERR_SHAPE;
-    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
-                                                                   (u32x2*)out);
+    launch_combine(y, inv, w, T, k, H, ksplit, T * k * H, out, st);
     return launch_status();
 }
 
@@ -1629,8 +1642,7 @@ static nvfp4_status moe_w4a16_unchecked(const void* x, const int32_t* ids, const
     if (s != NVFP4_OK)
         return s;
     // 4. combine (adds the planes of y in order)
-    combine_kernel<<<stream_grid(T * (H / 4), 8192), 256, 0, st>>>(y, inv, w, T, k, H, ksplit, T * k * H,
-                                                                   (u32x2*)out);
+    launch_combine(y, inv, w, T, k, H, ksplit, T * k * H, out, st);
     return launch_status();
 }
 

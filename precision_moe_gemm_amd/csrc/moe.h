@@ -368,43 +368,49 @@ NVFP4_DEV float4_t sum_planes(const float* p, int planes, int64_t plane)
 
 // out[t, 4c..4c+4) = bf16(sum_j w[t,j] * y[inv[t*k+j], 4c..4c+4)), j in
 // ascending order, where y is the sum (in plane order) of `planes` partial
-// planes `plane` floats apart.  The rows of four consecutive j are fetched
-// together.
+// planes `plane` floats apart.  A workgroup takes one token at a time (its
+// slot rows and weights read once, with scalar loads) and one slice of the
+// columns (blockIdx.y of col_split; several slices when the tokens alone
+// cannot fill the chip); each thread takes 4 columns per step and issues
+// the loads of all k slot rows together.
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
                const float* __restrict__ w, int64_t T, int k, int64_t H, int planes, int64_t plane,
-               u32x2* __restrict__ out)
+               int col_split, u32x2* __restrict__ out)
 {
     const int64_t groups = H / 4;
-    const int64_t total = T * groups;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-        const int64_t t = i / groups, c = i - t * groups;
-        float4_t acc = {0, 0, 0, 0};
-        for (int j0 = 0; j0 < k; j0 += 4) {
-            int32_t q[4];
-            float wt[4];
+    const int64_t per = (groups + col_split - 1) / col_split;
+    const int64_t g0 = (int64_t)blockIdx.y * per;
+    const int64_t g1 = g0 + per < groups ? g0 + per : groups;
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        for (int64_t g = g0 + threadIdx.x; g < g1; g += blockDim.x) {
+            float4_t acc = {0, 0, 0, 0};
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                int32_t q[8];
+                float wt[8];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const bool in = j0 + u < k;
-                q[u] = in ? inv[t * k + j0 + u] : -1;
-                wt[u] = in ? w[t * k + j0 + u] : 0.0f;
-            }
-            float4_t v[4];
+                for (int u = 0; u < 8; u++) {
+                    const bool in = j0 + u < k;
+                    q[u] = in ? const_load(inv, t * k + j0 + u) : -1;
+                    wt[u] = in ? const_load(w, t * k + j0 + u) : 0.0f;
+                }
+                float4_t v[8];
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                v[u] = q[u] >= 0 ? sum_planes(y + (int64_t)q[u] * H + 4 * c, planes, plane) : (float4_t){0, 0, 0, 0};
+                for (int u = 0; u < 8; u++)
+                    v[u] = q[u] >= 0 ? sum_planes(y + (int64_t)q[u] * H + 4 * g, planes, plane)
+                                     : (float4_t){0, 0, 0, 0};
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                if (q[u] >= 0) {
-                    acc.x += wt[u] * v[u].x;
-                    acc.y += wt[u] * v[u].y;
-                    acc.z += wt[u] * v[u].z;
-                    acc.w += wt[u] * v[u].w;
+                for (int u = 0; u < 8; u++) {
+                    if (q[u] >= 0) {
+                        acc.x += wt[u] * v[u].x;
+                        acc.y += wt[u] * v[u].y;
+                        acc.z += wt[u] * v[u].z;
+                        acc.w += wt[u] * v[u].w;
+                    }
                 }
             }
+            out[t * groups + g] = (u32x2){pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
         }
-        out[i] = (u32x2){pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
     }
 }
 

@@ -32,7 +32,7 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 // block scales)
 __device__ const float kMxOne = 1.0f;
 
-// ---- MXFP8 encode: one thread per 32-element block -----------------------
+// ---- MXFP8 encode: four lanes per 32-element block ------------------------
 // Block scale 2^e with e the smallest integer such that amax <= 448 * 2^e
 // (no element saturates), clamped to the UE8M0 range [-127, 127]; an
 // all-zero block takes e = 0.  Elements x * 2^-e rounded to E4M3 (nearest,
@@ -58,49 +58,64 @@ NVFP4_DEV int mx8_exponent(uint32_t amax_bits16)
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Work item = 8 elements (one 16-byte bf16 chunk, one 8-byte fp8 output):
+// consecutive lanes take consecutive chunks, so loads and stores are whole
+// lines per instruction, and the 4 lanes of a 32-element block share its
+// max with two lane swaps.  kU items per thread per trip, loads first.
+template <int kU>
 __global__ void __launch_bounds__(kMx8Threads)
 mxfp8_encode_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t blocks_per_row, int64_t ld_chunks,
-                    u32x4* __restrict__ out, uint8_t* __restrict__ e8m0)
+                    u32x2* __restrict__ out, uint8_t* __restrict__ e8m0)
 {
-    const int64_t nblk = rows * blocks_per_row;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-        const int64_t r = b / blocks_per_row;
-        const u32x4* src = x + r * ld_chunks + 4 * (b - r * blocks_per_row);
-        u32x4 v[4];
+    const int64_t cpr = 4 * blocks_per_row;  // 8-element chunks per row
+    const int64_t nq = rows * cpr;
+    const bool flat = ld_chunks == cpr;
+    constexpr int64_t kChunk = (int64_t)kU * kMx8Threads;
+    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < nq; base += (int64_t)gridDim.x * kChunk) {
+        u32x4 v[kU];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            v[i] = __builtin_nontemporal_load(src + i);
-        uint32_t am = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t m = absmax_bits8(v[i]);
-            am = am > m ? am : m;
+        for (int u = 0; u < kU; u++) {
+            int64_t h = base + u * kMx8Threads + threadIdx.x;
+            h = h < nq ? h : nq - 1;
+            int64_t src = h;
+            if (!flat) {
+                const int64_t r = h / cpr;
+                src = r * ld_chunks + (h - r * cpr);
+            }
+            v[u] = __builtin_nontemporal_load(x + src);
         }
-        const int e = mx8_exponent(am);
-        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);  // 2^-e (e in [-127, 127])
-        // 2^-e for e = -127 is 2^127: representable; e = 127 gives 2^-127, a
-        // subnormal fp32 whose exponent field is 0: build it from two factors
-        const float inv_lo = e == 127 ? 0x1p-64f : 1.0f;
-        const float inv_hi = e == 127 ? 0x1p-63f : inv;
-        uint32_t o[8];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        for (int u = 0; u < kU; u++) {
+            const int64_t h = base + u * kMx8Threads + threadIdx.x;
+            uint32_t am = absmax_bits8(v[u]);
+            uint32_t o = (uint32_t)__shfl_xor((int)am, 1, 64);
+            am = am > o ? am : o;
+            o = (uint32_t)__shfl_xor((int)am, 2, 64);
+            am = am > o ? am : o;
+            const int e = mx8_exponent(am);
+            const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);  // 2^-e (e in [-127, 127])
+            // 2^-e for e = -127 is 2^127: representable; e = 127 gives 2^-127, a
+            // subnormal fp32 whose exponent field is 0: build it from two factors
+            const float inv_lo = e == 127 ? 0x1p-64f : 1.0f;
+            const float inv_hi = e == 127 ? 0x1p-63f : inv;
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t q[2];
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const float f0 = __builtin_bit_cast(float, w[2 * h] << 16) * inv_hi * inv_lo;
-                const float f1 = __builtin_bit_cast(float, w[2 * h] & 0xFFFF0000u) * inv_hi * inv_lo;
-                const float f2 = __builtin_bit_cast(float, w[2 * h + 1] << 16) * inv_hi * inv_lo;
-                const float f3 = __builtin_bit_cast(float, w[2 * h + 1] & 0xFFFF0000u) * inv_hi * inv_lo;
-                uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-                p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
-                o[2 * i + h] = p;
+            for (int hh = 0; hh < 2; hh++) {
+                const float f0 = __builtin_bit_cast(float, w[2 * hh] << 16) * inv_hi * inv_lo;
+                const float f1 = __builtin_bit_cast(float, w[2 * hh] & 0xFFFF0000u) * inv_hi * inv_lo;
+                const float f2 = __builtin_bit_cast(float, w[2 * hh + 1] << 16) * inv_hi * inv_lo;
+                const float f3 = __builtin_bit_cast(float, w[2 * hh + 1] & 0xFFFF0000u) * inv_hi * inv_lo;
+                uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, pk, true);
+                q[hh] = pk;
+            }
+            if (h < nq) {
+                out[h] = (u32x2){q[0], q[1]};
+                if ((h & 3) == 0)
+                    e8m0[h >> 2] = (uint8_t)(e + 127);
             }
         }
-        out[2 * b] = (u32x4){o[0], o[1], o[2], o[3]};
-        out[2 * b + 1] = (u32x4){o[4], o[5], o[6], o[7]};
-        e8m0[b] = (uint8_t)(e + 127);
     }
 }
 
@@ -237,7 +252,9 @@ mx_w4a8_kernel(MxArgs p)
 #pragma unroll
     for (int j = 0; j < FN; j++)
         wsc[j] = wsexp + wrow(rw + 32 * j) * kb;
-    uint32_t sa[FM], sw[FN], na[FM], nw[FN];
+    // scale dwords of three groups in rotation (set G mod 3 holds group G's),
+    // so that a set is read only a group after its loads were issued
+    uint32_t sa[FM], sw[FN], ra3[3][FM], rw3[3][FN];
     auto load_scales = [&](int64_t G, uint32_t (&da)[FM], uint32_t (&dw)[FN]) {
         const int64_t g = G < ngr ? G : ngr - 1;
 #pragma unroll
@@ -247,15 +264,15 @@ mx_w4a8_kernel(MxArgs p)
         for (int j = 0; j < FN; j++)
             dw[j] = *(const uint32_t*)(wsc[j] + 4 * g);
     };
-    // this lane's blocks (q, 2 + q) of a group in bytes 0 and 2 (shifted
-    // only when used, so the loads stay in flight)
-    auto take_scales = [&]() {
+    // this lane's blocks (q, 2 + q) of a group in bytes 0 and 2, from set U
+    auto take_scales = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value % 3;
 #pragma unroll
         for (int i = 0; i < FM; i++)
-            sa[i] = na[i] >> (8 * q);
+            sa[i] = ra3[U][i] >> (8 * q);
 #pragma unroll
         for (int j = 0; j < FN; j++)
-            sw[j] = nw[j] >> (8 * q);
+            sw[j] = rw3[U][j] >> (8 * q);
     };
 
     float16_t acc[FM][FN];
@@ -298,36 +315,39 @@ mx_w4a8_kernel(MxArgs p)
             }
     };
 
-    // prologue: groups 0 and 1 staged, scales and k-step 0 fragments of
-    // group 0 in registers
-    load_scales(0, na, nw);
+    // prologue: groups 0 and 1 staged, the scales of groups 0 and 1 loaded,
+    // k-step 0 fragments of group 0 read
+    load_scales(0, ra3[0], rw3[0]);
+    load_scales(1, ra3[1], rw3[1]);
     issue(0, IntC<0>{});
     issue(1, IntC<1>{});
     wait_vm<0>();
     __syncthreads();
-    take_scales();
+    take_scales(IntC<0>{});
     read_frags(IntC<0>{}, IntC<0>{}, IntC<0>{});
     constexpr int NC = NJA + NJW;
-    // group G (T = G mod 3): scales of G + 1 and the copies of group G + 2
-    // (into the buffer group G - 1 used, free since the last barrier), then
-    // k-step 0 with the reads of k-step 1, the barrier that publishes group
-    // G + 1, k-step 1 with the reads of group G + 1's first fragments
+    // group G (T = G mod 3): the scales and the copies of group G + 2 (into
+    // the buffer group G - 1 used, free since the last barrier), then k-step
+    // 0 with the reads of k-step 1, the barrier that publishes group G + 1,
+    // k-step 1 with the reads of group G + 1's first fragments.  The scales
+    // of G + 1 were loaded a group earlier, so the wait before the barrier
+    // leaves both the scale loads and the copies of G + 2 in flight.
     auto group = [&](int64_t G, auto t) {
         constexpr int T = decltype(t)::value;
-        load_scales(G + 1, na, nw);
+        load_scales(G + 2, ra3[(T + 2) % 3], rw3[(T + 2) % 3]);
         issue(G + 2, IntC<(T + 2) % 3>{});
         __builtin_amdgcn_sched_barrier(0);
         mfmas(IntC<0>{}, IntC<0>{});
         read_frags(IntC<T>{}, IntC<1>{}, IntC<1>{});
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<NC>();  // group G + 1 and its scales (the copies of G + 2 may stay in flight)
+        wait_vm<NC + FM + FN>();  // group G + 1 (the scales and copies of G + 2 may stay in flight)
         wait_lgkm0();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
         mfmas(IntC<1>{}, IntC<1>{});
         read_frags(IntC<(T + 1) % 3>{}, IntC<0>{}, IntC<0>{});  // past the end: unused
         __builtin_amdgcn_sched_barrier(0);
-        take_scales();
+        take_scales(IntC<T + 1>{});
         __builtin_amdgcn_sched_barrier(0);
     };
     int64_t G = 0;

@@ -23,7 +23,10 @@ enum GlobalSource : int {
 };
 
 // ---- pass 1 of a dynamic global: partial max |x| per workgroup ----------
-// x is viewed as rows x (cols/8) chunks of 16 bytes.
+// x is viewed as rows x (cols/8) chunks of 16 bytes.  The pass walks the
+// tensor from its end to its start with ordinary (cached) loads, so that
+// when the encode pass then walks it from the start, its first part (up to
+// the size of the last-level cache) is still cached.
 __global__ void __launch_bounds__(kQuantThreads)
 amax_partials_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t chunks_per_row,
                      int64_t ld_chunks, uint32_t* __restrict__ partials)
@@ -34,12 +37,13 @@ amax_partials_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t chunks_p
     uint32_t m = 0;
     if (ld_chunks == chunks_per_row) {
         for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-            uint32_t a = absmax_bits8(__builtin_nontemporal_load(x + i));
+            uint32_t a = absmax_bits8(x[total - 1 - i]);
             m = m > a ? m : a;
         }
     } else {
         for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-            int64_t r = i / chunks_per_row, c = i - r * chunks_per_row;
+            const int64_t ir = total - 1 - i;
+            int64_t r = ir / chunks_per_row, c = ir - r * chunks_per_row;
             uint32_t a = absmax_bits8(x[r * ld_chunks + c]);
             m = m > a ? m : a;
         }
@@ -289,7 +293,7 @@ audit_kernel(const uint8_t* __restrict__ scales, int64_t n, unsigned long long* 
         atomicAdd(&counts[0], (unsigned long long)n);
 }
 
-// ---- optional data checks (nvfp4_set_checks): raise NVFP4_ERR_DATA ---------
+// ---- optional data checks// ---- optional data checks (nvfp4_set_checks): raise NVFP4_ERR_DATA ---------
 // E4M3 scale bytes: a NaN pattern (0x7F, 0xFF) or a set sign bit.
 __global__ void __launch_bounds__(kQuantThreads)
 check_scales_kernel(const uint8_t* __restrict__ s, int64_t n)

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("R,K,outliers", [(7, 256, 0.0), (300, 1024, 0.02), (33, 7168, 0.001)])
+@pytest.mark.parametrize("R,K,outliers", [(7, 256, 0.0), (300, 1024, 0.02), (33, 7168, 0.001), (3, 32, 0.0), (5, 96, 0.1)])
 def test_mxfp8_encode_matches_oracle(orc, R, K, outliers):
     x = synth.normal_bf16((R, K), 1.0, (830, R, K))
     if outliers:

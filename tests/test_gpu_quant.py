@@ -170,7 +170,7 @@ def test_host_errors():
     assert ei.value.status == 2
 
 
-@pytest.mark.parametrize("R,D,n", [(1000, 2560, 700), (37, 64, 5), (513, 16, 1031)])
+@pytest.mark.parametrize("R,D,n", [(1000, 2560, 700), (37, 64, 5), (513, 16, 1031), (200, 96, 333), (50, 48, 77)])
 def test_gather_dequantize_matches_oracle(orc, R, D, n):
     """Row gather-dequantize of an NVFP4 embedding table (rows of 2560 as in
     the n-gram table, plus small and ragged shapes): bit-exact against the

@@ -83,3 +83,36 @@ def test_noalloc_refuses_layers_beyond_the_scratch():
     step("noalloc: oversized layer refused")
     st, _ = _noalloc(x, ids, w, W)
     assert st == _lib.WORKSPACE
+
+
+def test_noalloc_layer_replays_from_a_hip_graph():
+    """The allocation-free layer captured in a HIP graph (it records no
+    allocation and no memset) and replayed several times, with eager work
+    and synchronizations in between: every replay equals the eager call."""
+    cfg = synth.C4_DECODE
+    W = workloads.build_moe_weights(cfg, DEV)
+    x = cfg.x(DEV)
+    ids, w = workloads.routing(cfg, DEV)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    ref = nv.nvfp4_moe_grouped_gemm(x, ids, w, W.w13, W.w2)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.nvfp4_moe_grouped_gemm_noalloc(x, ids, w, W.w13, W.w2, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    step("noalloc: capture the 384-expert decode layer")
+    with torch.cuda.graph(graph):
+        nv.nvfp4_moe_grouped_gemm_noalloc(x, ids, w, W.w13, W.w2, out=out)
+    for rep in range(4):
+        out.zero_()
+        # eager work on the same scratch between replays
+        other = nv.nvfp4_moe_grouped_gemm_noalloc(x[:8].contiguous(), ids[:8].contiguous(), w[:8].contiguous(),
+                                                  W.w13, W.w2)
+        torch.cuda.synchronize()
+        step(f"noalloc: graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        assert other.shape == (8, cfg.H)
+    assert nv.nvfp4_get_error() == 0
