@@ -141,9 +141,11 @@ nvfp4_status launch_quantize(QuantArgs a, int ntensors, hipStream_t st)
     return launch_status();
 }
 
+// With src == kGlobalPartials and pre_parts > 0, the partial maxima were
+// already written (pre_parts of them, by route_small_amax_kernel).
 nvfp4_status quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld, int src,
                            const void* gsrc, const nvfp4_tensor* out, int64_t row_off,
-                           uint32_t* partials, hipStream_t st)
+                           uint32_t* partials, hipStream_t st, int pre_parts = 0)
 {
     QuantArgs a{};
     a.x[0] = (const u32x4*)x;
@@ -155,7 +157,10 @@ nvfp4_status quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld
     a.blocks_per_row = cols / 16;
     a.ld_chunks = ld / 8;
     a.nparts = 0;
-    if (src == kGlobalPartials) {
+    if (src == kGlobalPartials && pre_parts > 0) {
+        a.gsrc[0] = partials;
+        a.nparts = pre_parts;
+    } else if (src == kGlobalPartials) {
         const int64_t chunks = rows * (cols / 8);
         const unsigned parts = stream_grid(chunks, kAmaxParts);
         amax_partials_kernel<<<parts, kQuantThreads, 0, st>>>((const u32x4*)x, rows, cols / 8, ld / 8, partials);
@@ -1503,12 +1508,24 @@ static nvfp4_status moe_grouped_gemm_impl(const void* x, const int32_t* ids, con
     const bool small = T * k <= kRouteSmall;
     const bool rag_gu = grouped_ragged(kModeGateUp, H, I), rag_dn = grouped_ragged(kModeDown, I, H);
     const int small_gu = grouped_all_small(T, H, gsplit, rag_gu), small_dn = grouped_all_small(T, I, ksplit, rag_dn);
-    if (small)
+    int pre_parts = 0;  // partial maxima of x written by the routing launch
+    if (small && !static_in_globals) {
+        // one launch: routing and both tile plans in block 0, the first pass
+        // of x's dynamic global in the others
+        pre_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kAmaxParts, ceil_div(T * (H / 8), 1024)));
+        route_small_amax_kernel<<<1 + pre_parts, 1024, 0, st>>>(
+            ids, (int)(T * k), E, offsets, perm, inv, hmax, at<int32_t>(ws, L.r.plan_gu),
+            grouped_small_bm(H, small_gu, T * k, E, rag_gu), small_gu, at<int32_t>(ws, L.r.plan_dn),
+            grouped_small_bm(I, small_dn, T * k, E, rag_dn), small_dn, (const u32x4*)x, T, H / 8, H / 8,
+            at<uint32_t>(ws, L.xparts));
+        s = launch_status();
+    } else if (small) {
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
                        grouped_small_bm(H, small_gu, T * k, E, rag_gu), small_gu, at<int32_t>(ws, L.r.plan_dn),
                        grouped_small_bm(I, small_dn, T * k, E, rag_dn), small_dn);
-    else
+    } else {
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st);
+    }
     if (s != NVFP4_OK)
         return s;
     // 2. quantize x once
@@ -1516,7 +1533,8 @@ static nvfp4_status moe_grouped_gemm_impl(const void* x, const int32_t* ids, con
     if (static_in_globals)
         s = quantize_impl(x, T, H, H, kGlobalStatic, static_in_globals, &xq, 0, nullptr, st);
     else
-        s = quantize_impl(x, T, H, H, kGlobalPartials, nullptr, &xq, 0, at<uint32_t>(ws, L.xparts), st);
+        s = quantize_impl(x, T, H, H, kGlobalPartials, nullptr, &xq, 0, at<uint32_t>(ws, L.xparts), st,
+                          pre_parts);
     if (s != NVFP4_OK)
         return s;
     // 3. gate_up + SwiGLU; with a static G_h the epilogue encodes h to NVFP4

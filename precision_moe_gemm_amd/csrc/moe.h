@@ -269,11 +269,10 @@ moe_plan_kernel(const int32_t* __restrict__ offsets, int E, int small_bm, int al
 // and zeroes `zero_word`, so a small layer needs one launch for all of it.
 constexpr int kRouteSmall = 1024;
 
-__global__ void __launch_bounds__(1024)
-route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
-                   int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
-                   int32_t* plan_gu, int small_bm_gu, int all_small_gu, int32_t* plan_dn, int small_bm_dn,
-                   int all_small_dn)
+NVFP4_DEV void route_small_block(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
+                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
+                                 int32_t* plan_gu, int small_bm_gu, int all_small_gu, int32_t* plan_dn,
+                                 int small_bm_dn, int all_small_dn)
 {
     __shared__ __attribute__((aligned(16))) int32_t sid[kRouteSmall];
     __shared__ int32_t off[kMaxExperts + 1];
@@ -345,6 +344,16 @@ route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* 
         plan_block(off, E, small_bm_gu, all_small_gu, plan_gu, lds16);
     if (plan_dn)
         plan_block(off, E, small_bm_dn, all_small_dn, plan_dn, lds16);
+}
+
+__global__ void __launch_bounds__(1024)
+route_small_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
+                   int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
+                   int32_t* plan_gu, int small_bm_gu, int all_small_gu, int32_t* plan_dn, int small_bm_dn,
+                   int all_small_dn)
+{
+    route_small_block(ids, npairs, E, offsets, perm, inv, zero_word, plan_gu, small_bm_gu, all_small_gu, plan_dn,
+                      small_bm_dn, all_small_dn);
 }
 
 // Sum over the `planes` partial planes (`plane` floats apart) of the four

@@ -53,6 +53,36 @@ amax_partials_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t chunks_p
         partials[blockIdx.x] = m << 16;  // bf16 magnitude bits -> float bits
 }
 
+// The routing of a small batch (block 0, one workgroup: route_small_block)
+// and the first pass of the activations' dynamic global (blocks 1..P: the
+// partial max |x| of a P-way split, as amax_partials_kernel) are
+// independent, so one launch of 1 + P workgroups serves both.
+__global__ void __launch_bounds__(1024)
+route_small_amax_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
+                        int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
+                        int32_t* plan_gu, int small_bm_gu, int all_small_gu, int32_t* plan_dn, int small_bm_dn,
+                        int all_small_dn, const u32x4* __restrict__ x, int64_t rows, int64_t chunks_per_row,
+                        int64_t ld_chunks, uint32_t* __restrict__ partials)
+{
+    if (blockIdx.x == 0) {
+        route_small_block(ids, npairs, E, offsets, perm, inv, zero_word, plan_gu, small_bm_gu, all_small_gu,
+                          plan_dn, small_bm_dn, all_small_dn);
+        return;
+    }
+    __shared__ uint32_t red[16];
+    const int64_t total = rows * chunks_per_row;
+    const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
+    uint32_t m = 0;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / chunks_per_row, c = i - r * chunks_per_row;
+        const uint32_t a = absmax_bits8(x[r * ld_chunks + c]);
+        m = m > a ? m : a;
+    }
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0)
+        partials[blockIdx.x - 1] = m << 16;  // bf16 magnitude bits -> float bits
+}
+
 // Global scale of a quantize launch (identical in every thread).
 NVFP4_DEV float load_global(int src, const void* gsrc, int nparts, uint32_t* lds16)
 {
