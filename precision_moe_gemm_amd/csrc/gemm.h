@@ -1034,10 +1034,11 @@ gemm_tile_kernel(GemmArgs p)
 // Epilogue of gemm_rtile_kernel, whose MFMAs take the W fragment as the
 // first operand: acc[i][j] is the transposed 32x32 fragment, lane l holding
 // output row 32 i + l % 32 of the wave tile and, in element 4 q + t, output
-// column 32 j + 8 q + 4 (l / 32) + t.  Each pass stages 128 bytes of every
-// wave row in this wave's own LDS region (TM rows; 16-byte slot s of row r at
-// slot s ^ (r % 8)) and writes whole 16-byte pieces: 8 lanes per row, 8 rows
-// per store instruction.
+// column 32 j + 8 q + 4 (l / 32) + t.  Each pass stages up to 128 bytes of
+// every wave row in this wave's own LDS region (TM rows; 16-byte slot s of row
+// r at slot s ^ (r % 8)) and writes whole 16-byte pieces: 8 lanes per row, 8
+// rows per store instruction (gate_up with 64-column wave tiles: 4 lanes per
+// row of 32 h columns, 16 rows).
 template <int BN, int TM, int TN, int FM, int FN, int MODE>
 NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float16_t (&acc)[FM][FN], int wave_m,
                             int wave_n, int lane, uint8_t* stg)
@@ -1057,8 +1058,10 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     if constexpr (MODE == kModeGateUp) {
-        // h = silu(gate) * up, bf16: TN / 2 = 64 columns (128 bytes) per row
-        static_assert(TN / 2 * 2 == 128, "one pass holds the wave's h columns");
+        // h = silu(gate) * up, bf16: TN / 2 columns (64 or 32: 128 or 64
+        // bytes) per wave row
+        constexpr int HS = TN / 16;  // 16-byte slots of h per wave row (64 or 32 columns)
+        static_assert(HS == 8 || HS == 4, "one pass holds the wave's h columns");
         const int64_t hcol0 = tc.nt * (BN / 2) + wave_n * (TN / 2);
         uint32_t hmax = 0;
 #pragma unroll
@@ -1087,8 +1090,8 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
             // h straight to NVFP4: each lane encodes whole 16-element blocks
             // (row b / 4, columns 16 (b % 4)) as the quantize kernel does
             const float Gh = *p.hq_global, six = 6.0f * Gh;
-            for (int b = lane; b < TM * 4; b += 64) {
-                const int r = b >> 2, c16 = b & 3;
+            for (int b = lane; b < TM * (HS / 2); b += 64) {
+                const int r = b / (HS / 2), c16 = b % (HS / 2);
                 if (r < rows_left) {
                     const u32x4 v0 = *(const u32x4*)slot(r, 2 * c16);
                     const u32x4 v1 = *(const u32x4*)slot(r, 2 * c16 + 1);
@@ -1103,11 +1106,13 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
             }
         } else {
             uint16_t* h = (uint16_t*)p.out;
+            constexpr int RPI = 64 / HS;  // rows per store instruction
+            const int hr = lane / HS, hs = lane % HS;
 #pragma unroll
-            for (int k = 0; k < TM / 8; k++) {
-                const int r = 8 * k + rl;
+            for (int k = 0; k < TM / RPI; k++) {
+                const int r = RPI * k + hr;
                 if (r < rows_left)
-                    *(u32x4*)(h + (wrow0 + r) * N + hcol0 + 8 * sl) = *(const u32x4*)slot(r, sl);
+                    *(u32x4*)(h + (wrow0 + r) * N + hcol0 + 8 * hs) = *(const u32x4*)slot(r, hs);
             }
             hmax = wave_max_u32(hmax);
             if (lane == 0 && hmax != 0)

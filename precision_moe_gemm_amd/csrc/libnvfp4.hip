@@ -221,6 +221,22 @@ nvfp4_status launch_tile(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
     return launch_status();
 }
 
+// The register-decode tile kernel alone, general weight scales (K a
+// multiple of 256).
+template <int BM, int BN, int MODE>
+nvfp4_status launch_rtile_general(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
+{
+    p.m_tiles = m_tiles_ub;
+    int64_t blocks = m_tiles_ub * p.n_tiles;
+    if (blocks == 0)
+        return NVFP4_OK;
+    blocks = ceil_div(blocks, 8) * 8;
+    if (blocks > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    gemm_rtile_kernel<BM, BN, MODE, false><<<(unsigned)blocks, 256, 0, st>>>(p);
+    return launch_status();
+}
+
 // The weight-streaming kernel serves A operands of at most 32 rows per
 // expert (on average; tiles of 16 or 32 rows) when K is a multiple of its
 // 256-element stage.
@@ -488,8 +504,18 @@ nvfp4_status dispatch_grouped(GemmArgs p, const int32_t* offsets, int64_t total_
     if (!all_small && total_rows > 64) {
         GemmArgs q = cls(1);
         q.ksplit = 1;
-        q.n_tiles = ceil_div(p.N, big_cols);
-        s = launch_tile<128, 256, MODE>(q, std::min<int64_t>(experts, total_rows / 65 + 1), st);
+        const int64_t m1 = std::min<int64_t>(experts, total_rows / 65 + 1);
+        if (!p.w_pow2 && p.K % 256 == 0) {
+            // general weight scales: the decode of both operands keeps the
+            // VALU as busy as the MFMA, and 128-column tiles (72 KB of LDS,
+            // 188 registers) run two workgroups per CU, so one wave's decode
+            // issues while the other's MFMA runs
+            q.n_tiles = ceil_div(p.N, big_cols / 2);
+            s = launch_rtile_general<128, 128, MODE>(q, m1, st);
+        } else {
+            q.n_tiles = ceil_div(p.N, big_cols);
+            s = launch_tile<128, 256, MODE>(q, m1, st);
+        }
         if (s != NVFP4_OK)
             return s;
     }
@@ -1508,16 +1534,20 @@ static nvfp4_status moe_grouped_gemm_impl(const void* x, const int32_t* ids, con
     const bool small = T * k <= kRouteSmall;
     const bool rag_gu = grouped_ragged(kModeGateUp, H, I), rag_dn = grouped_ragged(kModeDown, I, H);
     const int small_gu = grouped_all_small(T, H, gsplit, rag_gu), small_dn = grouped_all_small(T, I, ksplit, rag_dn);
+    nvfp4_tensor xq{at<uint8_t>(ws, L.xq_p), at<uint8_t>(ws, L.xq_s), at<float>(ws, L.gx), T, H, 1};
     int pre_parts = 0;  // partial maxima of x written by the routing launch
+    // a batch of at most kQuantSmall elements is quantized whole by that launch
+    const bool xq_fused = small && !static_in_globals && T * H <= kQuantSmall;
     if (small && !static_in_globals) {
         // one launch: routing and both tile plans in block 0, the first pass
-        // of x's dynamic global in the others
-        pre_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kAmaxParts, ceil_div(T * (H / 8), 1024)));
+        // of x's dynamic global (or all of x's quantize) in the others
+        pre_parts = xq_fused ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(kAmaxParts, ceil_div(T * (H / 8), 1024)));
         route_small_amax_kernel<<<1 + pre_parts, 1024, 0, st>>>(
             ids, (int)(T * k), E, offsets, perm, inv, hmax, at<int32_t>(ws, L.r.plan_gu),
             grouped_small_bm(H, small_gu, T * k, E, rag_gu), small_gu, at<int32_t>(ws, L.r.plan_dn),
             grouped_small_bm(I, small_dn, T * k, E, rag_dn), small_dn, (const u32x4*)x, T, H / 8, H / 8,
-            at<uint32_t>(ws, L.xparts));
+            at<uint32_t>(ws, L.xparts), xq_fused ? (uint32_t*)xq.packed : nullptr, xq_fused ? xq.scales : nullptr,
+            xq_fused ? xq.global : nullptr);
         s = launch_status();
     } else if (small) {
         s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, at<int32_t>(ws, L.r.plan_gu),
@@ -1528,11 +1558,10 @@ static nvfp4_status moe_grouped_gemm_impl(const void* x, const int32_t* ids, con
     }
     if (s != NVFP4_OK)
         return s;
-    // 2. quantize x once
-    nvfp4_tensor xq{at<uint8_t>(ws, L.xq_p), at<uint8_t>(ws, L.xq_s), at<float>(ws, L.gx), T, H, 1};
+    // 2. quantize x once (unless the routing launch did)
     if (static_in_globals)
         s = quantize_impl(x, T, H, H, kGlobalStatic, static_in_globals, &xq, 0, nullptr, st);
-    else
+    else if (!xq_fused)
         s = quantize_impl(x, T, H, H, kGlobalPartials, nullptr, &xq, 0, at<uint32_t>(ws, L.xparts), st,
                           pre_parts);
     if (s != NVFP4_OK)

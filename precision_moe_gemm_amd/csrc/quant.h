@@ -53,16 +53,56 @@ amax_partials_kernel(const u32x4* __restrict__ x, int64_t rows, int64_t chunks_p
         partials[blockIdx.x] = m << 16;  // bf16 magnitude bits -> float bits
 }
 
+// Dynamic-global quantize of a whole small tensor (at most kQuantSmall
+// elements, nhalf = elements / 8 half-blocks) by one workgroup of 1024
+// threads: thread t holds half-blocks t + 1024 u in v[u] (any value past the
+// end) and m_local, the largest magnitude bits among its valid ones.  The
+// workgroup max gives the global (written to gout), and every half-block is
+// encoded as quantize_kernel encodes it: lanes 2j and 2j + 1 hold the two
+// halves of one block.
+constexpr int kQuantSmall = 65536;
+constexpr int kQsU = kQuantSmall / 8 / 1024;  // half-blocks per thread
+
+NVFP4_DEV void encode_small_block(const u32x4 (&v)[kQsU], uint32_t m_local, int64_t nhalf,
+                                  uint32_t* __restrict__ packed, uint8_t* __restrict__ scales, float* gout,
+                                  uint32_t* red)
+{
+    const uint32_t m = block_max_u32(m_local, red);
+    const float G = global_from_amax(__uint_as_float(m << 16));
+    if (threadIdx.x == 0)
+        *gout = G;
+    const float six_g = 6.0f * G;
+#pragma unroll
+    for (int u = 0; u < kQsU; u++) {
+        const int64_t h = (int64_t)u * 1024 + threadIdx.x;
+        uint32_t am = absmax_bits8(v[u]);
+        const uint32_t other = (uint32_t)__shfl_xor((int)am, 1, 64);
+        am = am > other ? am : other;
+        uint32_t sc;
+        const float r = block_scale(am, G, six_g, &sc);
+        const uint32_t code = encode_half(v[u], r);
+        if (h < nhalf) {
+            packed[h] = code;
+            if ((h & 1) == 0)
+                scales[h >> 1] = (uint8_t)sc;
+        }
+    }
+}
+
 // The routing of a small batch (block 0, one workgroup: route_small_block)
 // and the first pass of the activations' dynamic global (blocks 1..P: the
 // partial max |x| of a P-way split, as amax_partials_kernel) are
-// independent, so one launch of 1 + P workgroups serves both.
+// independent, so one launch of 1 + P workgroups serves both.  With xq_packed
+// non-null (then P = 1 and rows * chunks_per_row <= kQuantSmall / 8), block 1
+// quantizes all of x itself: codes to xq_packed, scale bytes to xq_scales,
+// the global to xq_gout.
 __global__ void __launch_bounds__(1024)
 route_small_amax_kernel(const int32_t* __restrict__ ids, int npairs, int E, int32_t* __restrict__ offsets,
                         int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* zero_word,
                         int32_t* plan_gu, int small_bm_gu, int all_small_gu, int32_t* plan_dn, int small_bm_dn,
                         int all_small_dn, const u32x4* __restrict__ x, int64_t rows, int64_t chunks_per_row,
-                        int64_t ld_chunks, uint32_t* __restrict__ partials)
+                        int64_t ld_chunks, uint32_t* __restrict__ partials, uint32_t* __restrict__ xq_packed,
+                        uint8_t* __restrict__ xq_scales, float* xq_gout)
 {
     if (blockIdx.x == 0) {
         route_small_block(ids, npairs, E, offsets, perm, inv, zero_word, plan_gu, small_bm_gu, all_small_gu,
@@ -70,6 +110,24 @@ route_small_amax_kernel(const int32_t* __restrict__ ids, int npairs, int E, int3
         return;
     }
     __shared__ uint32_t red[16];
+    if (xq_packed) {
+        const int64_t nhalf = rows * chunks_per_row;
+        u32x4 v[kQsU];
+        uint32_t m = 0;
+#pragma unroll
+        for (int u = 0; u < kQsU; u++) {
+            const int64_t h = (int64_t)u * 1024 + threadIdx.x;
+            v[u] = (u32x4){0, 0, 0, 0};
+            if (h < nhalf) {
+                const int64_t r = h / chunks_per_row, c = h - r * chunks_per_row;
+                v[u] = x[r * ld_chunks + c];
+                const uint32_t a = absmax_bits8(v[u]);
+                m = m > a ? m : a;
+            }
+        }
+        encode_small_block(v, m, nhalf, xq_packed, xq_scales, xq_gout, red);
+        return;
+    }
     const int64_t total = rows * chunks_per_row;
     const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
     uint32_t m = 0;
