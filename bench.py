@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_moe384_T16384.jso
 # sources that shape the grouped gate_up launch (kernels, tile plan, class dispatch)
 GEMM_SOURCES = ["precision_moe_gemm_amd/csrc/gemm.h", "precision_moe_gemm_amd/csrc/common.h",
                 "precision_moe_gemm_amd/csrc/moe.h", "precision_moe_gemm_amd/csrc/libnvfp4.hip"]
-GROUPS = ("prefill", "gate_up", "quantize", "mlp", "mx", "c3", "decode", "mx_prefill", "gather", "kv")
+GROUPS = ("prefill", "gate_up", "quantize", "mlp", "mx", "c3", "decode", "mx_prefill", "gather", "kv", "ceiling")
 
 
 def log(msg):
@@ -64,7 +64,77 @@ def parse():
     ap.add_argument("--iters", type=int, default=10, help="timed iterations per breakdown row")
     ap.add_argument("--profile-copy", action="store_true",
                     help="also launch a 1 GiB plain copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the gate_up traffic summary from two rocprofv3 --pmc runs (FETCH_SIZE, "
+                         "WRITE_SIZE) of --only gate_up --profile-copy, then exit (no GPU use)")
     return ap.parse_args()
+
+
+# kernels of one nvfp4_moe_gate_up call on the 384-expert prefill layer
+TRAFFIC_KERNELS = {"moe_plan_kernel": r"moe_plan_kernel",
+                   "gemm_rtile_kernel<256,256,1,true>": r"gemm_rtile_kernel<256, 256, 1, true>",
+                   "gemm_rtile_kernel<128,256,1,true>": r"gemm_rtile_kernel<128, 256, 1, true>",
+                   "gemm_stream_kernel<1,true,false,16>": r"gemm_stream_kernel<1, true, false, 16>"}
+
+
+def _pmc_per_dispatch(d, counter):
+    """Mean per dispatch of `counter` (summed over its instances) for every
+    kernel in the rocprofv3 counter CSV under directory d; the copyBuffer
+    dispatches are kept apart (largest one)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out, copy = {}, 0.0
+    for name, short in TRAFFIC_KERNELS.items():
+        vals = [v for (k, _), v in per.items() if short in k]
+        if vals:
+            out[name] = sum(vals) / len(vals)
+    copies = [v for (k, _), v in per.items() if "copyBuffer" in k]
+    copy = max(copies) if copies else 0.0
+    return out, copy
+
+
+def write_traffic(fetch_dir, write_dir):
+    fetch, fcopy = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, wcopy = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    if not fcopy or not wcopy:
+        raise SystemExit("the 1 GiB calibration copy (--profile-copy) is missing from the counter runs")
+    gib = 1 << 30
+    ff, wf = gib / (fcopy * 1024), gib / (wcopy * 1024)
+    fb = sum(fetch.values()) * 1024 * ff
+    wb = sum(write.values()) * 1024 * wf
+    cmd = ("cd /tmp && TMPDIR=/tmp timeout -s KILL 150 rocprofv3 --pmc {c} --kernel-include-regex "
+           "'gemm_rtile_kernel|gemm_stream|moe_plan|copyBuffer' --output-format csv -d {d} -o p -- "
+           "python3 $R/bench.py --only gate_up --steps 2 --warmup 1 --profile-copy")
+    t = {"what": "HBM traffic of one grouped gate_up call (nvfp4_moe_gate_up) of the 384-expert top-8 layer at "
+                 "T=16384: tile plan + 256-row and 128-row register-decode tile kernels and the 16-row streaming "
+                 "kernel (power-of-two weight-scale variants)",
+         "commands": [cmd.format(c="FETCH_SIZE", d=fetch_dir), cmd.format(c="WRITE_SIZE", d=write_dir),
+                      f"python3 $R/bench.py --write-traffic {fetch_dir} {write_dir}"],
+         "fetch_kib_per_dispatch": {k: round(v, 1) for k, v in fetch.items()},
+         "write_kib_per_dispatch": {k: round(v, 1) for k, v in write.items()},
+         "calibration": {"kernel": "__amd_rocclr_copyBuffer, the 1 GiB copy of --profile-copy (largest dispatch)",
+                         "bytes_read": gib, "bytes_written": gib, "fetch_kib": fcopy, "write_kib": wcopy,
+                         "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+         "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+         "bytes_per_launch": int(fb + wb),
+         "algorithmic_bytes_per_launch_note": "minimum: gathered x rows 131072 x 7168 x 0.5625 B + touched "
+                                              "experts' w13 225 x 4096 x 7168 x 0.5625 B + h 131072 x 2048 x 2 B "
+                                              "= 4.77e9 B",
+         "source_hash": source_hash(), "sources": GEMM_SOURCES}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"bytes_per_launch": t["bytes_per_launch"], "file": TRAFFIC_FILE}))
 
 
 def source_hash():
@@ -162,6 +232,9 @@ def cpu_model():
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -472,7 +545,7 @@ def breakdown(args, timer, only=None):
     import torch
     res = {}
     it = args.iters
-    groups = [only] if only else ["quantize", "mlp", "mx", "c3", "decode", "mx_prefill", "gather", "kv"]
+    groups = [only] if only else ["quantize", "mlp", "mx", "c3", "decode", "mx_prefill", "gather", "kv", "ceiling"]
     for gname in groups:
         res.update(ROWS[gname](timer, it))
         torch.cuda.empty_cache()
@@ -732,8 +805,49 @@ def rows_kv(timer, it):
                                                                 "(2.5625 B/elem)")}
 
 
+def rows_ceiling(timer, it):
+    """Context, not hot-path rows: the read rate this GPU reaches on the
+    streaming GEMM's access patterns (csrc/probe/hbm_read.hip), over 778 MB of
+    weight-shaped rows (53 experts x 4096 rows x 3584 B, the decode batch's
+    touched gate_up codes) plus their 97 MB of scale bytes, a 512 MB flush
+    between passes."""
+    import ctypes
+    import torch
+    from precision_moe_gemm_amd import build
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    if not os.path.exists(build.PROBE_LIB):
+        raise SystemExit(f"{build.PROBE_LIB} not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.hbm_read_probe.restype = ctypes.c_int
+    lib.hbm_read_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    log("breakdown: HBM read ceiling of the streaming access patterns")
+    rows, rb = 53 * 4096, 3584
+    w = torch.zeros(rows * rb, dtype=torch.uint8, device=dev)
+    sc = torch.zeros(rows * rb // 8, dtype=torch.uint8, device=dev)
+    grid = 768  # the streaming GEMM's resident grid (3 workgroups per CU)
+    out = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    res = {}
+    for name, lanes, rbytes, with_sc in (("contiguous_16KB_per_stage", 256, 4096, False),
+                                         ("weight_tiles_128rows_x128B", 8, rb, False),
+                                         ("weight_tiles_plus_row_scales_16B", 8, rb, True)):
+        n = w.numel() // rbytes
+        n -= n % (128 if lanes == 8 else 4)
+        nbytes = n * rbytes + (n * rbytes // 8 if with_sc else 0)
+        args = (lanes, ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(sc.data_ptr() if with_sc else None), n, rbytes,
+                grid, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+        rc = lib.hbm_read_probe(*args)
+        if rc != 0:
+            raise SystemExit(f"hbm_read_probe({name}) failed: {rc}")
+        ms = timer(lambda: lib.hbm_read_probe(*args), it, flush=True)
+        res[f"hbm_read_{name}"] = row(ms, nbytes, bytes_basis=f"{nbytes / 1e6:.0f} MB read once")
+        log(f"breakdown: read {name}: {nbytes / ms / 1e9:.2f} TB/s")
+    return res
+
+
 ROWS = {"quantize": rows_quantize, "mlp": rows_mlp, "mx": rows_mx, "c3": rows_c3, "decode": rows_decode,
-        "mx_prefill": rows_mx_prefill, "gather": rows_gather, "kv": rows_kv}
+        "mx_prefill": rows_mx_prefill, "gather": rows_gather, "kv": rows_kv, "ceiling": rows_ceiling}
 
 
 if __name__ == "__main__":

@@ -140,13 +140,41 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The HBM read probe that bench.py times beside the kernels (the achievable
+# read rate of the streaming GEMM's access patterns); not part of libnvfp4.
+PROBE_SRC = os.path.join(HERE, "csrc", "probe", "hbm_read.hip")
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
+
+
+def start_probe_build():
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, PROBE_SRC]
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    proc.nvfp4_tmp = tmp
+    return proc
+
+
+def finish_probe_build(proc) -> str:
+    _, err = proc.communicate()
+    if proc.returncode != 0:
+        if os.path.exists(proc.nvfp4_tmp):
+            os.remove(proc.nvfp4_tmp)
+        err = "\n".join(l for l in err.splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError("probe build failed:\n" + err)
+    os.replace(proc.nvfp4_tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build_all(verbose: bool = False) -> str:
-    """The library and, concurrently, its sanitizer build (when stale)."""
+    """The library and, concurrently, its sanitizer build (when stale) and
+    the read probe."""
     proc = start_sanitized_build()
+    probe = start_probe_build()
     try:
         lib = build(verbose)
     finally:
         finish_sanitized_build(proc)
+        finish_probe_build(probe)
     return lib
 
 

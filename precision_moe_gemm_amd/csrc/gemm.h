@@ -200,8 +200,19 @@ NVFP4_DEV bool tile_coord(const GemmArgs& p, TileCoord& tc)
     const int64_t bid = xcd_item(m_act * p.n_tiles);
     if (bid < 0)
         return false;
-    const int64_t mt = bid / p.n_tiles;
-    tc.nt = bid - mt * p.n_tiles;
+    // Order of the logical tiles: bands of GM = 4 A tiles, and inside a band
+    // groups of GN (8, 7 or 4) W tiles with the A tile varying fastest.  The
+    // 32 tiles resident on an XCD at once then read about 4 A and 8 W tiles
+    // instead of 2 A and 16 (A tile fastest over all W tiles): the 384-expert
+    // prefill's 256-row class fetched 4.2 instead of 5.6 GB through L2.
+    const int64_t nt_all = p.n_tiles;
+    const int64_t GN = nt_all % 8 == 0 ? 8 : nt_all % 7 == 0 ? 7 : nt_all % 4 == 0 ? 4 : nt_all;
+    constexpr int64_t GM = 4;
+    const int64_t band = bid / (GM * nt_all), r = bid - band * GM * nt_all;
+    const int64_t gm = m_act - band * GM < GM ? m_act - band * GM : GM;
+    const int64_t ng = r / (gm * GN), q = r - ng * gm * GN;
+    const int64_t mt = band * GM + q % gm;
+    tc.nt = ng * GN + q / gm;
     tc.e = 0;
     if (MODE == kModeDense) {
         if (mt >= p.m_tiles)
