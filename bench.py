@@ -579,6 +579,7 @@ def rows_mlp(timer, it):
     c2 = synth.C2
     log("breakdown: dense MLP 5120/17408 as one expert")
     mlp = workloads.build_dense_mlp(c2, dev)
+    mlp_t = workloads.MoEWeights(nv.nvfp4_tile_scales(mlp.w13), nv.nvfp4_tile_scales(mlp.w2))
     res = {}
     for M in c2.Ms:
         x = c2.x(M, dev)
@@ -593,6 +594,11 @@ def rows_mlp(timer, it):
         if M <= 32:
             ms = timer(f, it, flush=True)
             res[f"dense_mlp_M{M}"] = row(ms, wbytes, flops, bytes_basis="NVFP4 weights, 0.5625 B/elem")
+            # weight scale bytes in the 128-row tiled order
+            ft = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, mlp_t.w13, mlp_t.w2, out=out, ws=ws)
+            ft()
+            res[f"dense_mlp_M{M}_tiled_scales"] = row(timer(ft, it, flush=True), wbytes, flops,
+                                                      bytes_basis="NVFP4 weights, 0.5625 B/elem")
         else:
             ms = timer(f, it)
             res[f"dense_mlp_M{M}"] = row(ms, None, flops)
@@ -668,6 +674,12 @@ def rows_decode(timer, it):
     f()
     res["moe_384e_top8_decode_T64"] = row(timer(f, it, flush=True), wbytes, bytes_basis=basis,
                                           experts_touched=int(len(touched)))
+    # the same experts with their scale bytes in the 128-row tiled order
+    # (prepared once, outside the timed region)
+    w13t, w2t = nv.nvfp4_tile_scales(W.w13), nv.nvfp4_tile_scales(W.w2)
+    f = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, w13t, w2t, out=out, ws=ws)
+    f()
+    res["moe_384e_top8_decode_T64_tiled_scales"] = row(timer(f, it, flush=True), wbytes, bytes_basis=basis)
     # calibrated globals (from one dynamic staged pass): h encoded in the epilogue
     xq4 = nv.nvfp4_quantize(x)
     perm4, off4, _ = nv.nvfp4_moe_route(ids, c4.E)
@@ -681,6 +693,10 @@ def rows_decode(timer, it):
     f = lambda: nv.nvfp4_moe_w4a16(x, ids, wt, W.w13, W.w2, out=out, ws=ws)
     f()
     res["moe_384e_top8_w4a16_decode_T64"] = row(timer(f, it, flush=True), wbytes, bytes_basis=basis)
+    f = lambda: nv.nvfp4_moe_w4a16(x, ids, wt, w13t, w2t, out=out, ws=ws)
+    f()
+    res["moe_384e_top8_w4a16_decode_T64_tiled_scales"] = row(timer(f, it, flush=True), wbytes, bytes_basis=basis)
+    del w13t, w2t
     (m13, e13), (m2, e2) = W.mx13, W.mx2
     mws = torch.empty(nv.nvfp4_workspace_size(_lib.OP_MX_MOE, c4.T, c4.k, c4.E, c4.H, c4.I), dtype=torch.uint8,
                       device=dev)

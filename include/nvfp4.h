@@ -10,7 +10,8 @@
  *                            bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6),
  *                            element 2j in the low nibble of byte j
  *   scales  uint8 [R, K/16]  one FP8 E4M3 (bias 7, max 448) block scale per
- *                            16 elements, row-major, no swizzle
+ *                            16 elements, row-major (weights may also
+ *                            be given in 128-row tiles: NVFP4_TILED_SCALES)
  *   global  float [1]        one FP32 per-tensor scale
  * and value = (e2m1 * scale) * global, i.e. 4.5 bits per element.  The three
  * buffers map onto a checkpoint's weight / weight_scale / weight_scale_2
@@ -97,6 +98,22 @@ typedef struct {
  * scales gives wrong results. */
 #define NVFP4_POW2_SCALES 1u
 
+/* nvfp4_tensor.flags: the scale bytes are stored in 128-row tiles instead of
+ * row-major (set by nvfp4_tile_scales; the values, codes and globals are the
+ * same).  For rows % 128 == 0 and cols % 256 == 0 only: scale byte b of row
+ * r of matrix m (b < cols/16) is at
+ *     m * rows * cols/16 + ((r/128 * cols/256 + b/16) * 128 + r%128) * 16 + b%16
+ * so the 16 bytes that 256 consecutive elements of each of 128 rows use are
+ * one contiguous 2 KB run.  A GEMM that streams a weight tile of 128 rows
+ * then reads its scales in whole cache lines instead of a 16-byte piece per
+ * row and stage.  This storage order is the library's own; the pages fix
+ * the scale (one E4M3 per 16 elements along the last dimension), not where
+ * it lives.  Accepted for the weight operand of nvfp4_gemm,
+ * nvfp4_gemm_w4a16 and the NVFP4 MoE entry points (w13, w2); every other
+ * tensor argument with this flag is refused (NVFP4_ERR_UNSUPPORTED), as is
+ * a tiled tensor whose shape breaks the rule above (NVFP4_ERR_SHAPE). */
+#define NVFP4_TILED_SCALES 2u
+
 /* Operations for nvfp4_workspace_size(). */
 enum {
     NVFP4_OP_QUANTIZE = 0, /* nvfp4_quantize                       */
@@ -152,6 +169,16 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* in, void* out, int32_t dtype, 
  */
 nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* ids, int64_t n,
                                      void* out, int32_t dtype, void* stream);
+
+/* Tile the scale bytes of `in` (row-major: flags without NVFP4_TILED_SCALES)
+ * into the 128-row order of NVFP4_TILED_SCALES, writing all
+ * in->batch * rows * cols/16 bytes to scales_out (device, caller-owned, 16-byte
+ * aligned, not overlapping in->scales).  The caller then describes the
+ * tensor with in->packed, scales_out, in->global and flags |
+ * NVFP4_TILED_SCALES.  For weights, done once when they are loaded.  Errors:
+ * NVFP4_ERR_SHAPE unless rows % 128 == 0 and cols % 256 == 0;
+ * NVFP4_ERR_INVALID_ARG for null or misaligned pointers or a tiled input. */
+nvfp4_status nvfp4_tile_scales(const nvfp4_tensor* in, uint8_t* scales_out, void* stream);
 
 /*
  * MXFP4 encode (OCP MX: blocks of 32 along the last dimension, UE8M0 scale

@@ -518,6 +518,27 @@ def audit_scales(t: NVFP4) -> dict:
 
 
 # --------------------------------------------------------------------------
+# 128-row tiled storage order of the scale bytes (a storage order of the
+# library's own, not a page's: the pages fix one E4M3 scale per 16 elements
+# along the last dimension, not where the bytes live)
+# --------------------------------------------------------------------------
+
+def tile_scales(scales: np.ndarray) -> np.ndarray:
+    """Scale bytes [batch, rows, cols/16] (row-major) -> the flat tiled
+    order: byte b of row r of matrix m goes to
+    m*rows*cols/16 + ((r//128 * cols/256 + b//16) * 128 + r%128) * 16 + b%16."""
+    s = np.asarray(scales, np.uint8)
+    if s.ndim == 2:
+        s = s[None]
+    B, R, NB = s.shape
+    if R % 128 or NB % 16:
+        raise OracleError(SHAPE, "tile_scales")
+    # [m, tile, rr, chunk, j] -> [m, tile, chunk, rr, j]
+    t = s.reshape(B, R // 128, 128, NB // 16, 16).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+# --------------------------------------------------------------------------
 # MX-native W4A8 routed experts (MXFP4 experts, MXFP8 activations)
 # --------------------------------------------------------------------------
 

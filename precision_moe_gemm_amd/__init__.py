@@ -22,7 +22,7 @@ __all__ = [
     "NVFP4Error", "NVFP4Tensor", "nvfp4_workspace_size", "nvfp4_quantize", "nvfp4_dequantize",
     "mxfp4_quantize", "mxfp4_to_nvfp4", "nvfp4_gemm", "nvfp4_moe_grouped_gemm", "nvfp4_moe_grouped_gemm_noalloc",
     "nvfp4_moe_route", "nvfp4_moe_gate_up", "nvfp4_moe_gate_up_q", "nvfp4_moe_down", "nvfp4_moe_combine",
-    "nvfp4_gather_dequantize", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8", "mx_moe_w4a8", "mx_moe_gate_up", "mx_moe_down",
+    "nvfp4_gather_dequantize", "nvfp4_tile_scales", "nvfp4_gemm_w4a16", "nvfp4_moe_w4a16", "mxfp8_quantize", "mx_gemm_w4a8", "mx_moe_w4a8", "mx_moe_gate_up", "mx_moe_down",
     "nvfp4_kv_quant", "nvfp4_kv_dequant", "nvfp4_audit_scales", "nvfp4_get_error", "nvfp4_set_checks",
     "nvfp4_recipe", "status_string",
 ]
@@ -144,6 +144,15 @@ def nvfp4_gather_dequantize(table: NVFP4Tensor, ids: torch.Tensor, dtype=torch.b
     _check(_lib.load().nvfp4_gather_dequantize(ctypes.byref(tc), _ptr(ids), n, _ptr(out), code,
                                                _stream(table.device)), "nvfp4_gather_dequantize")
     return out
+
+
+def nvfp4_tile_scales(t: NVFP4Tensor) -> NVFP4Tensor:
+    """The same tensor with its scale bytes in the 128-row tiled order
+    (NVFP4_TILED_SCALES): a new scales buffer; packed and global are shared."""
+    scales = torch.empty_like(t.scales)
+    tc = t.c()
+    _check(_lib.load().nvfp4_tile_scales(ctypes.byref(tc), _ptr(scales), _stream(t.device)), "nvfp4_tile_scales")
+    return NVFP4Tensor(t.packed, scales, t.global_, t.rows, t.cols, t.batch, t.flags | _lib.TILED_SCALES)
 
 
 def mxfp4_quantize(x: torch.Tensor):

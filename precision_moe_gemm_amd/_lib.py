@@ -35,6 +35,7 @@ class NVFP4TensorC(ctypes.Structure):
 
 
 POW2_SCALES = 1  # NVFP4_POW2_SCALES
+TILED_SCALES = 2  # NVFP4_TILED_SCALES
 
 
 # name -> (restype, argtypes); mirrors include/nvfp4.h
@@ -49,6 +50,7 @@ SIGNATURES = {
     "nvfp4_quantize": (ST, [P, I64, I64, I64, P, TP, P, SZ, P]),
     "nvfp4_dequantize": (ST, [TP, P, ctypes.c_int, P]),
     "nvfp4_gather_dequantize": (ST, [TP, P, I64, P, I32, P]),
+    "nvfp4_tile_scales": (ST, [TP, P, P]),
     "mxfp4_quantize": (ST, [P, I64, I64, I64, P, P, P]),
     "mxfp4_to_nvfp4": (ST, [P, P, I64, I64, I64, TP, P, SZ, P]),
     "nvfp4_gemm": (ST, [TP, TP, P, ctypes.c_int, P, SZ, P]),

@@ -74,6 +74,9 @@ struct GemmArgs {
     // every W block scale is a power of two (or zero): the scale is folded
     // into the fp4 -> f16 conversion
     int32_t w_pow2;
+    // W scale bytes in the 128-row tiled order (NVFP4_TILED_SCALES; then
+    // the W row count % 128 == 0 and K % 256 == 0)
+    int32_t w_tiled;
     // gate_up with a static G_h (non-null): h is encoded to NVFP4 in the
     // epilogue (codes [rows, N/2], scale bytes [rows, N/16]) instead of being
     // written as bf16 with its max
@@ -88,6 +91,18 @@ struct GemmArgs {
 
 // 16-byte chunk slot of chunk c in tile row r (8 chunks per row).
 NVFP4_DEV int chunk_slot(int r, int c) { return c ^ ((r ^ (r >> 1)) & 7); }
+
+// The 16 scale bytes of W row `row` (of its matrix) for the first 256
+// elements of K; those of the next 256 follow `w_scale_step` bytes on.
+// Row-major: row * K/16, step 16.  Tiled (NVFP4_TILED_SCALES): the 128-row
+// tile's 2 KB runs, one per 256 elements of K, step 2048.
+NVFP4_DEV const uint8_t* w_scale_row(const uint8_t* wsc, int64_t row, int64_t K, bool tiled)
+{
+    if (!tiled)
+        return wsc + row * (K / 16);
+    return wsc + ((row >> 7) * (K / 256) * 128 + (row & 127)) * 16;
+}
+NVFP4_DEV int64_t w_scale_step(bool tiled) { return tiled ? 2048 : 16; }
 
 // Two E4M3 bytes (byte 2*sel and 2*sel+1 of `w`) -> two f16 scales (exact).
 template <int kSel>
@@ -426,6 +441,7 @@ gemm_kernel(GemmArgs p)
     // ---- rows this thread decodes from packed codes ----------------------
     const uint8_t* csrc[RPT];
     const uint8_t* ssrc[RPT];
+    int64_t sstep[RPT];  // scale bytes from one group of 4 stages to the next
     int drow[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; i++) {
@@ -437,10 +453,13 @@ gemm_kernel(GemmArgs p)
             const int64_t ar = a_row_of(row);
             csrc[i] = p.a_packed + ar * kpb;
             ssrc[i] = p.a_scales + ar * kpsb;
+            sstep[i] = 16;
         } else {
             const int64_t wr = w_row_of(row - BM);
             csrc[i] = wp + wr * kpb;
-            ssrc[i] = wsc + wr * kpsb;
+            // (tiled W scales come with K % 256 == 0: whole groups, no RAG)
+            ssrc[i] = w_scale_row(wsc, wr, K, p.w_tiled);
+            sstep[i] = w_scale_step(p.w_tiled);
         }
     }
     u32x4 creg[2][RPT][2];
@@ -495,7 +514,7 @@ gemm_kernel(GemmArgs p)
         if (st0 + 4 <= nstages) {
 #pragma unroll
             for (int i = 0; i < RPT; i++)
-                tsc[i] = *(const u32x4*)(ssrc[i] + st0 * kStageScaleBytes);
+                tsc[i] = *(const u32x4*)(ssrc[i] + grp * sstep[i]);
         } else {
             const int64_t last = nstages - 1;
 #pragma unroll
@@ -1318,13 +1337,16 @@ gemm_rtile_kernel(GemmArgs p)
     // ---- scale copies: copy j of this wave fills 16-byte row slots
     // [64 (NS wave + j), +64) of a pair buffer with the 16 scale bytes of a
     // pair of groups (slots past the last row repeat it)
+    // (a copy's 64 rows are all A rows or all W rows: BM % 64 == 0)
     const uint8_t* ssrc[NS];
+    int64_t sstep[NS];  // scale bytes from one group pair to the next
 #pragma unroll
     for (int j = 0; j < NS; j++) {
         int r = 64 * (NS * wave + j) + lane;
         if (r >= ROWS)
             r = ROWS - 1;
-        ssrc[j] = (r < BM ? p.a_scales : wsc) + matrix_row(r) * kpsb;
+        ssrc[j] = r < BM ? p.a_scales + matrix_row(r) * kpsb : w_scale_row(wsc, matrix_row(r), K, p.w_tiled);
+        sstep[j] = r < BM ? 16 : w_scale_step(p.w_tiled);
     }
     // copies [J0, J1) of the codes of group G (clamped to the last) into buffer B
     auto issue_codes = [&](int64_t G, auto b_tag, auto j0_tag, auto j1_tag) {
@@ -1341,12 +1363,12 @@ gemm_rtile_kernel(GemmArgs p)
     };
     // the scale copies of group pair Q (clamped to the last) into pair buffer B
     auto issue_scales = [&](int64_t Q, auto b_tag) {
-        const int64_t sb = (Q < npr ? Q : npr - 1) * 16;
+        const int64_t q = Q < npr ? Q : npr - 1;
         uint8_t* dst = sbuf(b_tag);
 #pragma unroll
         for (int j = 0; j < NS; j++)
-            __builtin_amdgcn_global_load_lds((const void*)(ssrc[j] + sb), (lds_ptr_t)(dst + (NS * wave + j) * 1024),
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(ssrc[j] + q * sstep[j]),
+                                             (lds_ptr_t)(dst + (NS * wave + j) * 1024), 16, 0, 0);
     };
 
     // ---- this lane's fragment rows: A rows ra + 32 i, W rows rw + 32 j.
@@ -1691,6 +1713,7 @@ gemm_stream_kernel(GemmArgs p)
     const int64_t kpb = K / 2, kpsb = K / 16;
     const int nst_all = (int)(K / kSkBK);
     const int64_t w_rows = (MODE == kModeGateUp) ? 2 * p.N : p.N;
+    const int64_t ws_step = w_scale_step(p.w_tiled);  // W scale bytes per stage
 
     // item -> expert, A-side rows [row_begin, row_end), W tile, K split and
     // its stages [st0, st0 + nst)
@@ -1792,7 +1815,7 @@ gemm_stream_kernel(GemmArgs p)
             }
             ar = pv / p.topk;
         }
-        const uint8_t* wsrow = wsc + w_row_of(th & 127) * kpsb + t.st0 * (kSkBK / 16);
+        const uint8_t* wsrow = w_scale_row(wsc, w_row_of(th & 127), K, p.w_tiled) + t.st0 * ws_step;
         const uint8_t* apiece = p.a_packed + ar * kpb + t.st0 * (kSkBK / 2) + 16 * pc;
         xsrc = (!kAllA && loads_scales) ? wsrow : apiece;
         ssrc = wsrow;
@@ -1808,7 +1831,7 @@ gemm_stream_kernel(GemmArgs p)
     auto load_stage = [&](int64_t st, int set) {
         if (kAllA) {
             if (loads_scales)
-                sreg[set] = *(const u32x4*)(ssrc + st * (kSkBK / 16));
+                sreg[set] = *(const u32x4*)(ssrc + st * ws_step);
             if (A16) {
 #pragma unroll
                 for (int i = 0; i < 4; i++)
@@ -1822,7 +1845,7 @@ gemm_stream_kernel(GemmArgs p)
             for (int i = 0; i < 4; i++)
                 breg[set][i] = *(const u32x4*)(bsrc + st * kSkBK + 8 * i);
         } else {
-            const int64_t xo = loads_scales ? st * (kSkBK / 16) : st * (kSkBK / 2);
+            const int64_t xo = loads_scales ? st * ws_step : st * (kSkBK / 2);
             xreg[set] = *(const u32x4*)(xsrc + xo);
             if (!A16 && !loads_scales)
                 yreg[set] = *(const uint16_t*)(ysrc + st * (kSkBK / 16));

@@ -61,7 +61,10 @@ void launch_combine(const float* y, const int32_t* inv, const float* w, int64_t 
 }
 
 // An empty tensor (rows or cols 0) may carry null code/scale pointers.
-nvfp4_status check_tensor(const nvfp4_tensor* t, bool need_global = true)
+// Tensor argument checks.  Scale bytes in the 128-row tiled order
+// (NVFP4_TILED_SCALES) are taken only where `tiled_ok` (GEMM weight
+// operands), and only with whole 128-row, 256-column tiles.
+nvfp4_status check_tensor(const nvfp4_tensor* t, bool need_global = true, bool tiled_ok = false)
 {
     if (!t || (need_global && !t->global))
         return NVFP4_ERR_INVALID_ARG;
@@ -72,6 +75,14 @@ nvfp4_status check_tensor(const nvfp4_tensor* t, bool need_global = true)
         return NVFP4_ERR_SHAPE;
     if (!aligned(t->packed, 16) || !aligned(t->scales, 4) || (t->global && !aligned(t->global, 4)))
         return NVFP4_ERR_INVALID_ARG;
+    if (t->flags & NVFP4_TILED_SCALES) {
+        if (!tiled_ok)
+            return NVFP4_ERR_UNSUPPORTED;
+        if (t->rows % 128 != 0 || t->cols % 256 != 0)
+            return NVFP4_ERR_SHAPE;
+        if (!aligned(t->scales, 16))
+            return NVFP4_ERR_INVALID_ARG;
+    }
     return NVFP4_OK;
 }
 
@@ -201,6 +212,8 @@ nvfp4_status launch_gemm(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
 template <int BM, int BN, int MODE>
 nvfp4_status launch_tile(GemmArgs p, int64_t m_tiles_ub, hipStream_t st)
 {
+    if (p.w_tiled && p.K % 256 != 0)
+        return NVFP4_ERR_UNSUPPORTED;  // (tiled scales come with K % 256 == 0)
     p.m_tiles = m_tiles_ub;
     int64_t blocks = m_tiles_ub * p.n_tiles;
     if (blocks == 0)
@@ -985,6 +998,27 @@ nvfp4_status nvfp4_gather_dequantize(const nvfp4_tensor* table, const int32_t* i
     return s;
 }
 
+nvfp4_status nvfp4_tile_scales(const nvfp4_tensor* in, uint8_t* scales_out, void* stream)
+{
+    nvfp4_status s = check_tensor(in, false);
+    if (s != NVFP4_OK)
+        return s == NVFP4_ERR_UNSUPPORTED ? NVFP4_ERR_INVALID_ARG : s;  // (already tiled)
+    if (in->rows % 128 != 0 || in->cols % 256 != 0)
+        return NVFP4_ERR_SHAPE;
+    const int64_t bytes = in->batch * in->rows * (in->cols / 16);
+    if (bytes == 0)
+        return NVFP4_OK;
+    if (!scales_out || !aligned(scales_out, 16) || !aligned(in->scales, 16))
+        return NVFP4_ERR_INVALID_ARG;
+    const uint8_t *a = in->scales, *b = scales_out;
+    if (a < b + bytes && b < a + bytes)
+        return NVFP4_ERR_INVALID_ARG;  // the runs move: no in-place tiling
+    const int64_t n = bytes / 16;
+    tile_scales_kernel<<<stream_grid(n, 8192), 256, 0, S(stream)>>>((const u32x4*)in->scales, (u32x4*)scales_out,
+                                                                     in->rows, in->cols / 256, n);
+    return launch_status();
+}
+
 nvfp4_status mxfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* packed,
                             uint8_t* e8m0, void* stream)
 {
@@ -1045,7 +1079,7 @@ static nvfp4_status gemm_unchecked(const nvfp4_tensor* A, const nvfp4_tensor* W,
 {
     nvfp4_status s = check_tensor(A);
     if (s == NVFP4_OK)
-        s = check_tensor(W);
+        s = check_tensor(W, true, true);
     if (s != NVFP4_OK)
         return s;
     if (!C || (dtype != NVFP4_F32 && dtype != NVFP4_BF16))
@@ -1064,6 +1098,7 @@ static nvfp4_status gemm_unchecked(const nvfp4_tensor* A, const nvfp4_tensor* W,
     p.w_scales = W->scales;
     p.w_global = W->global;
     p.w_pow2 = (W->flags & NVFP4_POW2_SCALES) != 0;
+    p.w_tiled = (W->flags & NVFP4_TILED_SCALES) != 0;
     p.K = A->cols;
     p.M = A->rows;
     p.N = W->rows;
@@ -1095,7 +1130,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* W, void* C, i
 static nvfp4_status gemm_w4a16_unchecked(const void* a, int64_t M, int64_t K, int64_t lda, const nvfp4_tensor* W,
                               void* C, int32_t dtype, void* ws, size_t ws_bytes, void* stream)
 {
-    nvfp4_status s = check_tensor(W);
+    nvfp4_status s = check_tensor(W, true, true);
     if (s != NVFP4_OK)
         return s;
     if (!C || (dtype != NVFP4_F32 && dtype != NVFP4_BF16))
@@ -1115,6 +1150,7 @@ static nvfp4_status gemm_w4a16_unchecked(const void* a, int64_t M, int64_t K, in
     p.w_scales = W->scales;
     p.w_global = W->global;
     p.w_pow2 = (W->flags & NVFP4_POW2_SCALES) != 0;
+    p.w_tiled = (W->flags & NVFP4_TILED_SCALES) != 0;
     p.K = K;
     p.M = M;
     p.N = W->rows;
@@ -1309,7 +1345,7 @@ static nvfp4_status check_experts(const nvfp4_tensor* w13, const nvfp4_tensor* w
 {
     nvfp4_status s = NVFP4_OK;
     if (w13) {
-        s = check_tensor(w13);
+        s = check_tensor(w13, true, true);
         if (s != NVFP4_OK)
             return s;
         if (w13->batch != E || w13->rows % 2 != 0)
@@ -1318,7 +1354,7 @@ static nvfp4_status check_experts(const nvfp4_tensor* w13, const nvfp4_tensor* w
         *I = w13->rows / 2;
     }
     if (w2) {
-        s = check_tensor(w2);
+        s = check_tensor(w2, true, true);
         if (s != NVFP4_OK)
             return s;
         if (w2->batch != E)
@@ -1369,6 +1405,7 @@ static nvfp4_status moe_gate_up_impl(const nvfp4_tensor* xq, const int32_t* perm
     p.w_scales = w13->scales;
     p.w_global = w13->global;
     p.w_pow2 = (w13->flags & NVFP4_POW2_SCALES) != 0;
+    p.w_tiled = (w13->flags & NVFP4_TILED_SCALES) != 0;
     p.K = H;
     p.N = I;
     p.perm = perm;
@@ -1459,6 +1496,7 @@ static nvfp4_status moe_down_impl(const nvfp4_tensor* hq, const int32_t* offsets
     p.w_scales = w2->scales;
     p.w_global = w2->global;
     p.w_pow2 = (w2->flags & NVFP4_POW2_SCALES) != 0;
+    p.w_tiled = (w2->flags & NVFP4_TILED_SCALES) != 0;
     p.K = I;
     p.N = H;
     p.M = T * k;
@@ -1655,6 +1693,7 @@ static nvfp4_status moe_w4a16_unchecked(const void* x, const int32_t* ids, const
     p.w_scales = w13->scales;
     p.w_global = w13->global;
     p.w_pow2 = (w13->flags & NVFP4_POW2_SCALES) != 0;
+    p.w_tiled = (w13->flags & NVFP4_TILED_SCALES) != 0;
     p.K = H;
     p.N = I;
     p.M = T * k;
@@ -1677,6 +1716,7 @@ static nvfp4_status moe_w4a16_unchecked(const void* x, const int32_t* ids, const
     q.w_scales = w2->scales;
     q.w_global = w2->global;
     q.w_pow2 = (w2->flags & NVFP4_POW2_SCALES) != 0;
+    q.w_tiled = (w2->flags & NVFP4_TILED_SCALES) != 0;
     q.K = I;
     q.N = H;
     q.M = T * k;
@@ -1832,7 +1872,7 @@ nvfp4_status nvfp4_kv_dequant(const nvfp4_tensor* k_cache, const nvfp4_tensor* v
 
 nvfp4_status nvfp4_audit_scales(const nvfp4_tensor* t, int64_t* counts, void* stream)
 {
-    nvfp4_status s = check_tensor(t, false);
+    nvfp4_status s = check_tensor(t, false, true);
     if (s != NVFP4_OK)
         return s;
     if (!counts || !aligned(counts, 8))

@@ -427,4 +427,20 @@ __global__ void zero_u64_kernel(unsigned long long* p, int n)
         p[threadIdx.x] = 0;
 }
 
+// Scale bytes, row-major [batch][rows][chunks * 16] -> the 128-row tiled
+// order [batch][rows/128][chunks][128][16] (chunks = K / 256): output run o
+// (16 bytes) takes input run (m, 128 t + rr, c) for o = ((m * rows/128 + t) *
+// chunks + c) * 128 + rr, so the writes are contiguous.
+__global__ void __launch_bounds__(256)
+tile_scales_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out, int64_t rows, int64_t chunks, int64_t n)
+{
+    const int64_t tiles = rows / 128;
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < n; o += (int64_t)gridDim.x * 256) {
+        const int64_t rr = o & 127, q = o >> 7;
+        const int64_t c = q % chunks, mt = q / chunks;
+        const int64_t t = mt % tiles, m = mt / tiles;
+        out[o] = in[(m * rows + 128 * t + rr) * chunks + c];
+    }
+}
+
 }  // namespace nvfp4

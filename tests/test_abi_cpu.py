@@ -123,6 +123,38 @@ def test_host_validation_fails_before_launch(lib):
                               None) == _lib.SHAPE
 
 
+def test_tiled_scale_rules_fail_before_launch(lib):
+    """NVFP4_TILED_SCALES: whole 128-row x 256-column tiles only, weight
+    operands only, and the conversion refuses bad shapes, tiled inputs and
+    overlapping buffers, all on the host."""
+    from precision_moe_gemm_amd import _lib
+    TL = _lib.TILED_SCALES
+    # conversion: rows % 128, cols % 256
+    assert lib.nvfp4_tile_scales(ctypes.byref(_lib.NVFP4TensorC(16, 16, 16, 64, 256, 1)), ctypes.c_void_p(4096),
+                                 None) == _lib.SHAPE
+    assert lib.nvfp4_tile_scales(ctypes.byref(_lib.NVFP4TensorC(16, 16, 16, 128, 128, 1)), ctypes.c_void_p(4096),
+                                 None) == _lib.SHAPE
+    # an already tiled input, an overlapping output, a misaligned output
+    assert lib.nvfp4_tile_scales(ctypes.byref(_lib.NVFP4TensorC(16, 16, 16, 128, 256, 1, TL)),
+                                 ctypes.c_void_p(1 << 20), None) == _lib.INVALID_ARG
+    assert lib.nvfp4_tile_scales(ctypes.byref(_lib.NVFP4TensorC(16, 4096, 16, 128, 256, 1)),
+                                 ctypes.c_void_p(4096 + 1024), None) == _lib.INVALID_ARG
+    assert lib.nvfp4_tile_scales(ctypes.byref(_lib.NVFP4TensorC(16, 4096, 16, 128, 256, 1)),
+                                 ctypes.c_void_p(1 << 20 | 4), None) == _lib.INVALID_ARG
+    # tiled tensors outside weight operands are refused
+    t = _lib.NVFP4TensorC(16, 16, 16, 128, 256, 1, TL)
+    assert lib.nvfp4_dequantize(ctypes.byref(t), ctypes.c_void_p(16), 0, None) == _lib.UNSUPPORTED
+    assert lib.nvfp4_gather_dequantize(ctypes.byref(t), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 0,
+                                       None) == _lib.UNSUPPORTED
+    W = _lib.NVFP4TensorC(16, 16, 16, 128, 256, 1)
+    assert lib.nvfp4_gemm(ctypes.byref(t), ctypes.byref(W), ctypes.c_void_p(16), 0, None, 0,
+                          None) == _lib.UNSUPPORTED
+    # a tiled weight with a partial 128-row tile -> shape
+    W3 = _lib.NVFP4TensorC(16, 16, 16, 96, 256, 1, TL)
+    A = _lib.NVFP4TensorC(16, 16, 16, 4, 256, 1)
+    assert lib.nvfp4_gemm(ctypes.byref(A), ctypes.byref(W3), ctypes.c_void_p(16), 0, None, 0, None) == _lib.SHAPE
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from precision_moe_gemm_amd import _lib
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -302,3 +302,29 @@ def test_audit_counts_planted_bytes(orc):
     t = orc.NVFP4(np.zeros((3, 96), np.uint8), s, 1.0)
     a = orc.audit_scales(t)
     assert a == AUDIT_EXPECT
+
+
+def test_tile_scales_matches_the_index_rule(orc):
+    """The tiled scale order against its defining index rule, byte by byte
+    (plain loops, two matrices of 256 x 512): every byte lands where the rule
+    puts it, so the permutation is one to one; a wrong stride, a transposed
+    tile or a mixed-up matrix offset would misplace some byte."""
+    rng = np.random.default_rng(11)
+    B, R, C = 2, 256, 512
+    s = rng.integers(0, 256, (B, R, C // 16), dtype=np.uint8)
+    t = orc.tile_scales(s)
+    assert t.shape == (B * R * C // 16,)
+    want = np.zeros_like(t)
+    hit = np.zeros(t.size, np.int32)
+    for m in range(B):
+        for r in range(R):
+            for b in range(C // 16):
+                o = m * R * (C // 16) + ((r // 128 * (C // 256) + b // 16) * 128 + r % 128) * 16 + b % 16
+                want[o] = s[m, r, b]
+                hit[o] += 1
+    assert (hit == 1).all()
+    np.testing.assert_array_equal(t, want)
+    # a tile's first 2 KB run: the 16 bytes of 256 elements of rows 0..127
+    np.testing.assert_array_equal(t[:2048].reshape(128, 16), s[0, :128, :16])
+    with pytest.raises(orc.OracleError):
+        orc.tile_scales(s[:, :200])
