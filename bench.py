@@ -265,11 +265,12 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ctx)
     if not args.no_extras:
-        static_res = ctx.pop("static_res")
+        static_res, tiled_res = ctx.pop("static_res"), ctx.pop("tiled_res")
         ctx.clear()
         torch.cuda.empty_cache()
         result["breakdown"] = breakdown(args, timer)
         result["breakdown"]["moe_384e_prefill_static_globals"] = static_res
+        result["breakdown"]["moe_384e_prefill_tiled_scales"] = tiled_res
     print(json.dumps(result), flush=True)
 
 
@@ -394,7 +395,21 @@ def headline(args, timer, dev, stream):
         log(f"MoE prefill, static globals: {sms:.3f} ms/step")
         static_res = row(sms, flops=flops, globals="G_x, G_h = amax/2688 of this input (calibrated); h "
                                                    "encoded in the gate_up epilogue")
-    ctx = dict(cfg=cfg, x=x, perm=perm, offsets=offsets, static_res=static_res)
+    # ---- the same layer with the experts' scale bytes in the 128-row tiled
+    # order (prepared once, outside the timed region) ----
+    tiled_res = None
+    if not args.no_extras:
+        w13t, w2t = nv.nvfp4_tile_scales(W.w13), nv.nvfp4_tile_scales(W.w2)
+
+        def step_tiled():
+            nv.nvfp4_moe_grouped_gemm(x, ids, w, w13t, w2t, out=out, ws=ws)
+
+        step_tiled()
+        tms = timer(step_tiled, max(5, args.steps))
+        log(f"MoE prefill, tiled weight scales: {tms:.3f} ms/step")
+        tiled_res = row(tms, flops=flops, weights="scale bytes in the 128-row tiled order")
+        del w13t, w2t
+    ctx = dict(cfg=cfg, x=x, perm=perm, offsets=offsets, static_res=static_res, tiled_res=tiled_res)
     return result, ctx
 
 
@@ -646,7 +661,13 @@ def rows_c3(timer, it):
     ms = timer(f, it, flush=True)
     flops = 2.0 * c3.T * c3.k * 3 * c3.H * c3.I
     wbytes = c3.E * 3 * c3.H * c3.I * 0.5625
-    return {"moe_512e_top10_T4096": row(ms, wbytes, flops, bytes_basis="all 512 experts' NVFP4 weights")}
+    w13t, w2t = nv.nvfp4_tile_scales(W.w13), nv.nvfp4_tile_scales(W.w2)
+    f = lambda: nv.nvfp4_moe_grouped_gemm(x, ids, wt, w13t, w2t, out=out, ws=ws)
+    f()
+    mst = timer(f, it, flush=True)
+    return {"moe_512e_top10_T4096": row(ms, wbytes, flops, bytes_basis="all 512 experts' NVFP4 weights"),
+            "moe_512e_top10_T4096_tiled_scales": row(mst, wbytes, flops,
+                                                     bytes_basis="all 512 experts' NVFP4 weights")}
 
 
 def rows_decode(timer, it):
@@ -836,8 +857,8 @@ def rows_ceiling(timer, it):
         raise SystemExit(f"{build.PROBE_LIB} not built: run __graft_entry__.build()")
     lib = ctypes.CDLL(build.PROBE_LIB)
     lib.hbm_read_probe.restype = ctypes.c_int
-    lib.hbm_read_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
-                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.hbm_read_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     log("breakdown: HBM read ceiling of the streaming access patterns")
     rows, rb = 53 * 4096, 3584
     w = torch.zeros(rows * rb, dtype=torch.uint8, device=dev)
@@ -845,14 +866,15 @@ def rows_ceiling(timer, it):
     grid = 768  # the streaming GEMM's resident grid (3 workgroups per CU)
     out = torch.empty(grid * 256, dtype=torch.int32, device=dev)
     res = {}
-    for name, lanes, rbytes, with_sc in (("contiguous_16KB_per_stage", 256, 4096, False),
-                                         ("weight_tiles_128rows_x128B", 8, rb, False),
-                                         ("weight_tiles_plus_row_scales_16B", 8, rb, True)):
+    for name, lanes, rbytes, with_sc, sc_tiled in (("contiguous_16KB_per_stage", 256, 4096, False, 0),
+                                                   ("weight_tiles_128rows_x128B", 8, rb, False, 0),
+                                                   ("weight_tiles_plus_row_scales_16B", 8, rb, True, 0),
+                                                   ("weight_tiles_plus_tiled_scales_2KB", 8, rb, True, 1)):
         n = w.numel() // rbytes
         n -= n % (128 if lanes == 8 else 4)
         nbytes = n * rbytes + (n * rbytes // 8 if with_sc else 0)
-        args = (lanes, ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(sc.data_ptr() if with_sc else None), n, rbytes,
-                grid, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+        args = (lanes, ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(sc.data_ptr() if with_sc else None), sc_tiled,
+                n, rbytes, grid, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
         rc = lib.hbm_read_probe(*args)
         if rc != 0:
             raise SystemExit(f"hbm_read_probe({name}) failed: {rc}")

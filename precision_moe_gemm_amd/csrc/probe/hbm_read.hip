@@ -9,7 +9,9 @@
 //   L = 256 with 4096-byte rows: 16 KB contiguous per stage (a plain stream)
 //   L = 8: 128 rows x 128 bytes per stage (the streaming GEMM's code loads)
 // With `scales` non-null the 128-row tiles also read 16 scale bytes of every
-// row per stage from a [rows, row_bytes / 8] array (its scale-byte loads).
+// row per stage from a [rows, row_bytes / 8] array (its scale-byte loads):
+// row-major (16 bytes of each of 128 rows), or in the 128-row tiled order
+// (one 2 KB run per tile and stage).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,8 +21,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int L>
 __global__ void __launch_bounds__(256)
-read_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc, int ntiles, int nst, int64_t row_bytes,
-            uint32_t* __restrict__ out)
+read_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc, int sc_tiled, int ntiles, int nst,
+            int64_t row_bytes, uint32_t* __restrict__ out)
 {
     constexpr int RP = 256 / L;  // rows per load instruction round
     constexpr int R = 4 * RP;    // rows per tile
@@ -39,7 +41,8 @@ read_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc, int n
         for (int j = 0; j < 4; j++)
             dst[j] = *(const u32x4*)(base + (int64_t)j * RP * row_bytes);
         if (sc && tid < R)
-            sdst = *(const u32x4*)(sc + ((int64_t)ltile * R + tid) * sc_bytes + (int64_t)ls * 16);
+            sdst = sc_tiled ? *(const u32x4*)(sc + ((int64_t)ltile * nst + ls) * 2048 + tid * 16)
+                            : *(const u32x4*)(sc + ((int64_t)ltile * R + tid) * sc_bytes + (int64_t)ls * 16);
         if (++ls == nst) {
             // next tile of this workgroup; past the last, reread the last stage
             ls = 0;
@@ -79,12 +82,13 @@ read_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc, int n
 
 // Launch one read pass on `stream`.  lanes_per_row is 8 (128-row tiles) or
 // 256 (4-row tiles of whole 4096-byte rows); rows * row_bytes bytes at w; sc
-// null or rows * row_bytes / 8 bytes (lanes_per_row 8 only); out holds grid *
+// null or rows * row_bytes / 8 bytes (lanes_per_row 8 only), in the tiled
+// order when sc_tiled is non-zero; out holds grid *
 // 256 words.  Returns 0, or -1 for a shape the kernel does not take (rows not
 // a whole number of tiles, row_bytes not a whole number of stages, grid
 // outside [8, 4096]), or the HIP error of the launch.
-extern "C" int hbm_read_probe(int lanes_per_row, const void* w, const void* sc, int64_t rows, int64_t row_bytes,
-                              int grid, void* out, void* stream)
+extern "C" int hbm_read_probe(int lanes_per_row, const void* w, const void* sc, int sc_tiled, int64_t rows,
+                              int64_t row_bytes, int grid, void* out, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
     if (grid < 8 || grid > 4096 || rows <= 0 || row_bytes <= 0 || !w || !out)
@@ -92,12 +96,12 @@ extern "C" int hbm_read_probe(int lanes_per_row, const void* w, const void* sc, 
     if (lanes_per_row == 8) {
         if (rows % 128 != 0 || row_bytes % 128 != 0 || row_bytes % 8 != 0)
             return -1;
-        read_kernel<8><<<grid, 256, 0, st>>>((const uint8_t*)w, (const uint8_t*)sc, (int)(rows / 128),
+        read_kernel<8><<<grid, 256, 0, st>>>((const uint8_t*)w, (const uint8_t*)sc, sc_tiled, (int)(rows / 128),
                                              (int)(row_bytes / 128), row_bytes, (uint32_t*)out);
     } else if (lanes_per_row == 256) {
         if (rows % 4 != 0 || row_bytes != 4096 || sc)
             return -1;
-        read_kernel<256><<<grid, 256, 0, st>>>((const uint8_t*)w, nullptr, (int)(rows / 4), 1, row_bytes,
+        read_kernel<256><<<grid, 256, 0, st>>>((const uint8_t*)w, nullptr, 0, (int)(rows / 4), 1, row_bytes,
                                                (uint32_t*)out);
     } else {
         return -1;
