@@ -1144,8 +1144,10 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
                 if (r < rows_left)
                     *(u32x4*)(h + (wrow0 + r) * N + hcol0 + 8 * hs) = *(const u32x4*)slot(r, hs);
             }
-            hmax = wave_max_u32(hmax);
-            if (lane == 0 && hmax != 0)
+            // one atomic per workgroup: the four waves meet in LDS first
+            __shared__ uint32_t red[16];
+            hmax = block_max_u32(hmax, red);
+            if (threadIdx.x == 0 && hmax != 0)
                 atomicMax(p.h_amax, hmax << 16);
         }
     } else {
@@ -2100,8 +2102,10 @@ gemm_stream_kernel(GemmArgs p)
     if (g < total)
         iter(IntC<1>{});
     if (MODE == kModeGateUp && p.ksplit == 1 && !p.hq_global) {
-        hmax = wave_max_u32(hmax);
-        if (lane == 0 && hmax != 0)
+        // one atomic per workgroup (the waves meet in the idle scale staging):
+        // all workgroups finish together, and same-address atomics serialize
+        hmax = block_max_u32(hmax, (uint32_t*)lds_ws[0]);
+        if (tid == 0 && hmax != 0)
             atomicMax(p.h_amax, hmax << 16);
     }
     wait_vm<0>();  // the rereads past the last item
@@ -2144,8 +2148,12 @@ swiglu_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t rows
         const uint32_t mag = hb & 0x7FFFu;
         hmax = hmax > mag ? hmax : mag;
     }
-    hmax = wave_max_u32(hmax);
-    if ((threadIdx.x & 63) == 0 && hmax != 0)
+    if (hq_global)
+        return;
+    // one atomic per workgroup: same-address atomics serialize
+    __shared__ uint32_t red[16];
+    hmax = block_max_u32(hmax, red);
+    if (threadIdx.x == 0 && hmax != 0)
         atomicMax(h_amax, hmax << 16);
 }
 

@@ -264,15 +264,36 @@ int64_t stream_slots(int bm) { return bm == kSkBM ? 768 : 512; }
 
 // K split of the dense weight-streaming GEMM: at most one workgroup per
 // resident slot, at least four stages per split, partials <= 32 MiB.
+// K split of `tiles` streaming work items over `slots` resident workgroups,
+// at most smax ways: the split that minimises the finishing time, counted
+// as rounds of items (ceil(tiles * s / slots)) times the item length (1 / s),
+// the smaller split on a tie.  A persistent grid finishes when its busiest
+// workgroup does, so 272 tiles on 512 slots take one full item unsplit, two
+// half items split in two, but two thirds of an item split in three.
+int64_t balanced_split(int64_t tiles, int64_t slots, int64_t smax)
+{
+    if (tiles <= 0 || tiles >= slots * 2 / 3 || smax <= 1)
+        return 1;
+    int64_t best = 1;
+    double best_t = (double)ceil_div(tiles, slots);
+    for (int64_t s = 2; s <= smax; s++) {
+        const double t = (double)ceil_div(tiles * s, slots) / (double)s;
+        if (t < best_t - 1e-9) {
+            best = s;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 int gemm_ksplit(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || !use_stream_gemm(M, K))
         return 1;
     const int64_t base = ceil_div(M, stream_bm(M)) * ceil_div(N, kSkBN);
-    int64_t s = stream_slots(stream_bm(M)) / base;
-    s = std::min<int64_t>(s, K / kSkBK / 4);
-    s = std::min<int64_t>(s, ((int64_t)32 << 20) / (M * N * 4));
-    return (int)std::max<int64_t>(1, s);
+    int64_t smax = std::min<int64_t>(K / kSkBK / 4, ((int64_t)32 << 20) / (M * N * 4));
+    smax = std::min<int64_t>(smax, stream_slots(stream_bm(M)));
+    return (int)balanced_split(base, stream_slots(stream_bm(M)), smax);
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K)
@@ -350,8 +371,9 @@ nvfp4_status launch_stream_gemm(GemmArgs p, int64_t m_tiles_ub, int bm, hipStrea
     if (s != NVFP4_OK || p.ksplit <= 1 || MODE == kModeDown)
         return s;  // grouped down: the combine adds the planes
     if (MODE == kModeGateUp) {
+        // (at most 256 workgroups: each adds one same-address atomic)
         const int64_t cnt = p.M * p.N;
-        const unsigned rb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(2048, ceil_div(cnt, 256)));
+        const unsigned rb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(256, ceil_div(cnt, 256)));
         swiglu_reduce_kernel<<<rb, 256, 0, st>>>(p.partial, p.ksplit, p.M, p.N, (uint16_t*)p.out, p.h_amax,
                                                  p.hq_global, p.hq_packed, p.hq_scales);
         return launch_status();
@@ -429,12 +451,9 @@ int moe_down_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
         return 1;
     const int bm = grouped_small_bm(I, 1, np, E);
     const int64_t tiles = small_tiles_est(np, E, bm) * ceil_div(H, kSkBN);
-    if (tiles >= stream_slots(bm) * 2 / 3)
-        return 1;
-    int64_t s = stream_slots(bm) / tiles;
-    s = std::min<int64_t>(s, I / kSkBK / 4);
-    s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * H * 4));
-    return (int)std::max<int64_t>(1, s);
+    int64_t smax = std::min<int64_t>(I / kSkBK / 4, ((int64_t)64 << 20) / (np * H * 4));
+    smax = std::min<int64_t>(smax, stream_slots(bm));
+    return (int)balanced_split(tiles, stream_slots(bm), smax);
 }
 
 // K split of the fused gate_up projection of a tiny batch (as the down
@@ -449,12 +468,10 @@ int moe_gate_ksplit(int64_t T, int32_t k, int32_t E, int64_t H, int64_t I)
         return 1;
     const int bm = grouped_small_bm(H, 1, np, E);
     const int64_t tiles = small_tiles_est(np, E, bm) * ceil_div(I, kSkBN / 2);
-    if (tiles >= stream_slots(bm) * 2 / 3)
-        return 1;
-    int64_t s = stream_slots(bm) / tiles;
-    s = std::min<int64_t>(s, H / kSkBK / 4);
-    s = std::min<int64_t>(s, ((int64_t)64 << 20) / (np * 2 * I * 4));
-    return (int)std::max<int64_t>(1, s);
+    // the partial gate and up planes stay within 16 MB
+    int64_t smax = std::min<int64_t>(H / kSkBK / 4, ((int64_t)16 << 20) / (np * 2 * I * 4));
+    smax = std::min<int64_t>(smax, stream_slots(bm));
+    return (int)balanced_split(tiles, stream_slots(bm), smax);
 }
 
 // Grouped projections: plan the tiles of every class on the device, then
