@@ -702,9 +702,58 @@ nvfp4_status launch_mx_grouped_class(MxArgs q, int64_t m_tiles_ub, hipStream_t s
 // no expert could fill a larger tile; any ids are still covered).
 int mx_all_small(int64_t T) { return T <= 64 ? 1 : 0; }
 
+// Rows of the MX layer's small tiles: 32-row weight-streaming tiles when
+// every row takes small tiles and both projections' K (H, and I) are
+// multiples of the 256-element stage (H always is), else 64-row tiles of the
+// tile kernel.  One plan serves both projections.
+int mx_small_bm(int64_t T, int64_t I) { return (mx_all_small(T) && I % kMsBK == 0) ? kMsBM : 64; }
+
+// Workgroups of the MX streaming kernel the device holds at once (a multiple
+// of 8; one query per mode and device, cached as stream_resident caches).
+template <int MODE>
+int64_t mx_stream_resident()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        dev = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mx_stream_kernel<MODE>, 256, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 8;
+        v = std::max(8, per_cu * cus / 8 * 8);
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// The 32-row weight-streaming class of an MX projection: items of (A tile,
+// 64 h columns (gate_up) or 128 W rows), a resident grid.
+template <int MODE>
+nvfp4_status launch_mx_stream(MxArgs q, int64_t m_tiles_ub, hipStream_t st)
+{
+    if (q.K % kMsBK != 0)
+        return NVFP4_ERR_SHAPE;
+    q.m_tiles = m_tiles_ub;
+    q.n_tiles = ceil_div(q.N, MODE == kModeGateUp ? 64 : kMsBN);
+    const int64_t items = m_tiles_ub * q.n_tiles;
+    if (items == 0)
+        return NVFP4_OK;
+    if (items > 0x7FFFFFFF)
+        return NVFP4_ERR_SHAPE;
+    const int64_t blocks = std::min(ceil_div(items, 8) * 8, mx_stream_resident<MODE>());
+    mx_stream_kernel<MODE><<<(unsigned)blocks, 256, 0, st>>>(q);
+    return launch_status();
+}
+
 // One grouped MX projection over the plan's classes: 256-row tiles, one
 // 128-row tile for a remainder of 65-128 rows, one 64-row tile for at most 64
-// (only the last when every row takes small tiles).
+// (only the last when every row takes small tiles; then 32-row streaming
+// tiles instead when K allows, as mx_small_bm decides for the plan).
 template <int MODE>
 nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t T, int64_t total_rows, int32_t E, hipStream_t st)
 {
@@ -718,6 +767,9 @@ nvfp4_status mx_grouped(MxArgs p, const int32_t* plan, int64_t T, int64_t total_
         return q;
     };
     nvfp4_status s = NVFP4_OK;
+    const int64_t I = MODE == kModeGateUp ? p.N : p.K;
+    if (mx_small_bm(T, I) == kMsBM)
+        return launch_mx_stream<MODE>(cls(kPlanSmall), total_rows / kMsBM + std::min<int64_t>(E, total_rows), st);
     if (mx_all_small(T))
         return launch_mx_grouped_class<64, MODE>(cls(kPlanSmall), total_rows / 64 + std::min<int64_t>(E, total_rows), st);
     if (total_rows > 128)
@@ -737,7 +789,7 @@ nvfp4_status mx_moe_gate_up_impl(const uint8_t* xq, const uint8_t* xe, const int
                                  hipStream_t st)
 {
     if (!plan_ready) {
-        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, mx_all_small(T), plan);
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, mx_small_bm(T, I), mx_all_small(T), plan);
         nvfp4_status s = launch_status();
         if (s != NVFP4_OK)
             return s;
@@ -763,7 +815,7 @@ nvfp4_status mx_moe_down_impl(const uint8_t* hq, const uint8_t* he, const int32_
                               int32_t* plan, bool plan_ready, hipStream_t st)
 {
     if (!plan_ready) {
-        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, mx_all_small(T), plan);
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, mx_small_bm(T, I), mx_all_small(T), plan);
         nvfp4_status s = launch_status();
         if (s != NVFP4_OK)
             return s;
@@ -1321,7 +1373,7 @@ nvfp4_status mx_moe_w4a8(const void* x, const int32_t* ids, const float* w, int6
     // projections (64-row small tiles)
     if ((s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st)) != NVFP4_OK)
         return s;
-    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, 64, mx_all_small(T), plan);
+    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, mx_small_bm(T, I), mx_all_small(T), plan);
     if ((s = launch_status()) != NVFP4_OK)
         return s;
     // 2. x -> MXFP8 (token order)

@@ -372,4 +372,271 @@ mx_w4a8_kernel(MxArgs p)
                                            (wave < 2 ? lds_a0 : lds_a1) + (wave & 1) * TM * 128);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming W4A8 for decode batches (at most 32 rows per A tile).
+//
+// The structure of the NVFP4 weight-streaming kernel (gemm_stream_kernel):
+// a resident grid whose workgroups walk (A tile, W tile) items with one
+// register pipeline three 256-element stages deep, each stage staged in LDS
+// behind one barrier; but no decode: the scaled MFMA (32x32x64, E2M1 x E4M3
+// with one E8M0 scale per 32 elements of each operand) reads both operands
+// from LDS as stored.  A workgroup owns 128 W rows, one 32-row fragment per
+// wave, and up to 32 A rows.  Per stage each thread loads 4 pieces of W
+// codes (8 lanes per 128-byte row segment), 2 pieces of A (16 lanes per
+// 256-byte row segment) and, for 128 + 32 threads, the 8 scale bytes of a W
+// or A row.  In gate_up mode the rows of a fragment alternate four gate and
+// four up rows of the same 16 output columns: the MFMA puts rows 8 j + 4 q +
+// [0, 4) of the weight fragment in lane half q, so lane l holds gate and
+// lane l + 32 up of the same (token, column) and one lane swap forms h.
+// ---------------------------------------------------------------------------
+constexpr int kMsBK = 256;   // K elements per stage
+constexpr int kMsBN = 128;   // W rows per workgroup
+constexpr int kMsBM = 32;    // A rows per tile
+
+template <int MODE>
+__global__ void __launch_bounds__(256)
+mx_stream_kernel(MxArgs p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][kMsBN * 128];  // E2M1 codes, 2 x 16 KB
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kMsBM * 256];  // E4M3, 2 x 8 KB
+    __shared__ __attribute__((aligned(16))) uint32_t lds_sw[2][kMsBN * 2];  // W scale bytes, 8 per row
+    __shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][kMsBM * 2];  // A scale bytes, 8 per row
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 5, fr = lane & 31;
+
+    // ---- items (A tile fastest), dealt as gemm_stream_kernel deals them:
+    // XCD x owns a contiguous eighth, round-robin over its workgroups
+    const int m_act = const_load(p.tile_off, p.experts);
+    const int items = m_act * (int)p.n_tiles;
+    const int per = (items + 7) >> 3;
+    const int x_begin = (int)(blockIdx.x & 7) * per;
+    const int x_end = x_begin + per < items ? x_begin + per : items;
+    if (x_begin >= x_end)
+        return;
+    const int active = (int)(gridDim.x >> 3), slot = (int)(blockIdx.x >> 3);
+    if (x_begin + slot >= x_end)
+        return;
+
+    const int64_t K = p.K, kpb = K / 2, kb = K / 32;
+    const int nst = (int)(K / kMsBK);
+    const int64_t w_rows = MODE == kModeGateUp ? 2 * p.N : p.N;
+
+    struct Item {
+        int64_t row_begin, row_end, nt;
+        int e;
+    };
+    auto item_of = [&](int it) {
+        Item t;
+        const int mt = (int)((uint32_t)it % (uint32_t)m_act);
+        t.nt = (int)((uint32_t)it / (uint32_t)m_act);
+        int lo = 0, hi = p.experts - 1;  // largest e with tile_off[e] <= mt
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (const_load(p.tile_off, mid) <= mt)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        t.e = lo;
+        t.row_begin = const_load(p.row_base, lo) + (int64_t)(mt - const_load(p.tile_off, lo)) * kMsBM;
+        const int64_t eend = const_load(p.row_lim, lo);
+        t.row_end = t.row_begin + kMsBM < eend ? t.row_begin + kMsBM : eend;
+        return t;
+    };
+    // W row (within the expert) of tile row r (wave r / 32, fragment row
+    // r % 32); gate_up: fragment row rho holds column 16 wave + (rho % 4) +
+    // 4 (rho / 8), from the gate half when (rho / 4) is even, else the up half
+    auto w_row_of = [&](const Item& t, int r) -> int64_t {
+        if (MODE == kModeGateUp) {
+            const int rho = r & 31;
+            const int64_t c = t.nt * 64 + 16 * (r >> 5) + (rho & 3) + 4 * (rho >> 3);
+            return ((rho >> 2) & 1) ? p.N + c : c;
+        }
+        const int64_t n = t.nt * kMsBN + r;
+        return n < p.N ? n : p.N - 1;  // (a ragged last tile rereads a valid row, never stored)
+    };
+
+    // ---- this thread's loads: W pieces j (tile row 32 j + tid / 8, piece
+    // tid % 8), A pieces j (tile row 16 j + tid / 16, piece tid % 16), and
+    // the scale bytes of W row tid (tid < 128) or A row tid - 128
+    const uint8_t* wsrc[4];
+    const uint8_t* asrc[2];
+    const uint8_t* ssrc;
+    auto setup_loads = [&](const Item& t) {
+        int th = tid;
+        asm volatile("" : "+v"(th));  // formed here, once per item (see gemm_stream_kernel)
+        const uint8_t* wp = p.w + (int64_t)t.e * w_rows * kpb;
+        const uint8_t* wsc = p.w_sc + (int64_t)t.e * w_rows * kb;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            wsrc[j] = wp + w_row_of(t, 32 * j + (th >> 3)) * kpb + 16 * (th & 7);
+        auto a_row = [&](int r) -> int64_t {
+            int64_t q_ = t.row_begin + r;
+            if (q_ >= t.row_end)
+                q_ = t.row_begin;  // padding rows repeat a valid row; never stored
+            if (MODE == kModeGateUp)
+                return const_load(p.perm, q_) / p.topk;
+            return q_;
+        };
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            asrc[j] = p.a + a_row(16 * j + (th >> 4)) * K + 16 * (th & 15);
+        ssrc = th < kMsBN ? wsc + w_row_of(t, th) * kb : p.a_sc + a_row((th - kMsBN) & 31) * kb;
+    };
+
+    u32x4 wreg[3][4], areg[3][2];
+    u32x2 sreg[3];
+    const bool loads_sc = tid < kMsBN + kMsBM;
+    auto load_stage = [&](int st, int set) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            wreg[set][j] = *(const u32x4*)(wsrc[j] + (int64_t)st * (kMsBK / 2));
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            areg[set][j] = *(const u32x4*)(asrc[j] + (int64_t)st * kMsBK);
+        if (loads_sc)
+            sreg[set] = *(const u32x2*)(ssrc + (int64_t)st * (kMsBK / 32));
+    };
+    auto store_stage = [&](int set, int b) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int r = 32 * j + (tid >> 3);
+            *(u32x4*)(&lds_w[b][r * 128 + 16 * sk_wslot(r, tid & 7)]) = wreg[set][j];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int r = 16 * j + (tid >> 4);
+            *(u32x4*)(&lds_a[b][r * 256 + 16 * ((tid & 15) ^ (r & 15))]) = areg[set][j];
+        }
+        if (tid < kMsBN)
+            *(u32x2*)(&lds_sw[b][2 * tid]) = sreg[set];
+        else if (loads_sc)
+            *(u32x2*)(&lds_sa[b][2 * (tid - kMsBN)]) = sreg[set];
+    };
+
+    float16_t acc = (float16_t){};
+    // k-steps S = 0..3 of the stage in buffer b: the wave's W fragment row
+    // fr of block 2 S + q (16 bytes of codes) and A row fr's elements
+    // [16 q, +16) of blocks 2 S and 2 S + 1; scale byte 2 S + q of each row
+    auto compute = [&](int b) {
+        const int rw = 32 * wave + fr;
+        const uint32_t* swr = &lds_sw[b][2 * rw];
+        const uint32_t* sar = &lds_sa[b][2 * fr];
+#pragma unroll
+        for (int S = 0; S < 4; S++) {
+            const u32x4 w = *(const u32x4*)(&lds_w[b][rw * 128 + 16 * sk_wslot(rw, 2 * S + q)]);
+            const u32x4 lo = *(const u32x4*)(&lds_a[b][fr * 256 + 16 * ((4 * S + q) ^ (fr & 15))]);
+            const u32x4 hi = *(const u32x4*)(&lds_a[b][fr * 256 + 16 * ((4 * S + 2 + q) ^ (fr & 15))]);
+            const uint32_t sw = swr[S >> 1] >> (8 * q), sa = sar[S >> 1] >> (8 * q);
+            const v8i_t wv = (v8i_t){(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+            const v8i_t av = (v8i_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                                     (int)hi.w};
+            if (S & 1)
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc, 4, 0, 2, (int)sw, 2, (int)sa);
+            else
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc, 4, 0, 0, (int)sw, 0, (int)sa);
+        }
+    };
+
+    // ---- epilogue of item t: lane l holds token row fr and, in element i,
+    // fragment row (i % 4) + 8 (i / 4) + 4 q ---------------------------------
+    uint32_t hmax = 0;
+    auto epilogue = [&](const Item& t) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int fr_ = ln & 31, q_ = ln >> 5;
+        const int rows_left = (int)(t.row_end - t.row_begin);
+        const int64_t row = t.row_begin + fr_;
+        if (MODE == kModeGateUp) {
+            // lane half 0: gate, half 1: up, of columns 16 wave + i
+            float up[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                up[i] = __shfl_xor(acc[i], 32, 64);
+            if (q_ == 0 && fr_ < rows_left) {
+                uint32_t hv[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const uint32_t h0 = f32_to_bf16(silu_f(acc[2 * i]) * up[2 * i]);
+                    const uint32_t h1 = f32_to_bf16(silu_f(acc[2 * i + 1]) * up[2 * i + 1]);
+                    hv[i] = h0 | (h1 << 16);
+                    const uint32_t m0 = h0 & 0x7FFFu, m1 = h1 & 0x7FFFu;
+                    hmax = hmax > m0 ? hmax : m0;
+                    hmax = hmax > m1 ? hmax : m1;
+                }
+                uint16_t* h = (uint16_t*)p.out + row * p.N + t.nt * 64 + 16 * wave;
+                *(u32x4*)h = (u32x4){hv[0], hv[1], hv[2], hv[3]};
+                *(u32x4*)(h + 8) = (u32x4){hv[4], hv[5], hv[6], hv[7]};
+            }
+        } else if (fr_ < rows_left) {
+            // columns 32 wave + 8 j + 4 q + [0, 4)
+            const int64_t col0 = t.nt * kMsBN + 32 * wave + 4 * q_;
+            float* y = (float*)p.out + row * p.N + col0;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                if (col0 + 8 * j < p.N)
+                    *(float4_t*)(y + 8 * j) = (float4_t){acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+        }
+    };
+
+    // ---- load cursor three stages ahead of the compute cursor; past the
+    // last item it rereads that item's last stage (never computed) -------------
+    int l_it = x_begin + slot, l_s = 0;
+    setup_loads(item_of(l_it));
+    auto load_next = [&](int set) {
+        load_stage(l_s, set);
+        if (++l_s == nst) {
+            if (l_it + active < x_end) {
+                l_it += active;
+                setup_loads(item_of(l_it));
+                l_s = 0;
+            } else {
+                l_s = nst - 1;
+            }
+        }
+    };
+    int c_it = x_begin + slot, c_s = 0;
+    int total = 0;
+    for (int it = c_it; it < x_end; it += active)
+        total += nst;
+    load_next(0);
+    load_next(1);
+    load_next(2);
+    store_stage(0, 0);
+    __syncthreads();
+    int g = 0;
+    auto iter = [&](auto set_tag) {
+        constexpr int cur = decltype(set_tag)::value;
+        constexpr int nxt = (cur + 1) % 3;
+        store_stage(nxt, (g + 1) & 1);
+        load_next(cur);
+        compute(g & 1);
+        __syncthreads();
+        g++;
+        if (++c_s == nst) {
+            epilogue(item_of(c_it));
+            acc = (float16_t){};
+            c_it += active;
+            c_s = 0;
+        }
+    };
+    while (g + 3 <= total) {
+        iter(IntC<0>{});
+        iter(IntC<1>{});
+        iter(IntC<2>{});
+    }
+    if (g < total)
+        iter(IntC<0>{});
+    if (g < total)
+        iter(IntC<1>{});
+    if (MODE == kModeGateUp) {
+        hmax = block_max_u32(hmax, &lds_sw[0][0]);
+        if (tid == 0 && hmax != 0)
+            atomicMax(p.h_amax, hmax << 16);
+    }
+    wait_vm<0>();  // the rereads past the last item
+}
+
 }  // namespace nvfp4

@@ -112,13 +112,34 @@ def test_mx_moe_all_tile_classes_sampled(orc):
 
 
 def test_mx_moe_decode_batch(orc):
-    """A decode-sized batch over many experts: every row in 64-row tiles."""
+    """A decode-sized batch over many experts: every row in 32-row
+    weight-streaming tiles (mx_stream_kernel)."""
     _check_mx_moe(orc, synth.MoE(seed=52, E=64, k=8, H=512, I=256, T=16))
+
+
+@pytest.mark.parametrize("cfg", [
+    synth.MoE(seed=54, E=16, k=4, H=2048, I=512, T=48, zipf=1.1),  # 8 / 2 stages, experts of 1-45 rows
+    synth.MoE(seed=55, E=8, k=2, H=512, I=256, T=1),               # one token
+], ids=["skewed-many-stages", "one-token"])
+def test_mx_moe_streaming_every_row(orc, cfg):
+    """The streaming class with several 256-element stages per item (the
+    register pipeline crosses items), experts holding more than one 32-row
+    tile, and a single token; every row checked."""
+    _check_mx_moe(orc, cfg)
+
+
+def test_mx_moe_streaming_repeated_ids(orc):
+    """All 120 pairs to one expert with I = 256: four 32-row streaming tiles
+    of one expert, every row checked."""
+    cfg = synth.MoE(seed=56, E=4, k=3, H=256, I=256, T=40)
+    ids = torch.full((cfg.T, cfg.k), 1, dtype=torch.int32)
+    _check_mx_moe(orc, cfg, ids=ids)
 
 
 def test_mx_moe_repeated_ids_decode_batch(orc):
     """A small batch whose pairs all go to one expert (ids repeated within a
-    token): 120 rows of one expert in 64-row tiles, every row checked."""
+    token): 120 rows of one expert in 64-row tiles (I = 128 is not a whole
+    streaming stage), every row checked."""
     cfg = synth.MoE(seed=53, E=4, k=3, H=256, I=128, T=40)
     ids = torch.full((cfg.T, cfg.k), 2, dtype=torch.int32)
     _check_mx_moe(orc, cfg, ids=ids)
