@@ -2125,6 +2125,39 @@ swiglu_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t rows
     const int64_t plane = rows * 2 * N;
     const float Gh = hq_global ? *hq_global : 1.0f, six = 6.0f * Gh;
     uint32_t hmax = 0;
+    if (!hq_global && N % 4 == 0 && count < ((int64_t)1 << 31)) {
+        // bf16 h: four consecutive columns per thread (16-byte loads, the
+        // planes' loads four at a time, added in the same split order)
+        const uint32_t n4 = (uint32_t)(N / 4), count4 = (uint32_t)(count / 4);
+        for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count4; i += gridDim.x * blockDim.x) {
+            const uint32_t r = i / n4, c = 4 * (i - r * n4);
+            const float* g = partial + (int64_t)r * 2 * N + c;
+            float4_t gg = *(const float4_t*)g, uu = *(const float4_t*)(g + N);
+            for (int s0 = 1; s0 < ksplit; s0 += 4) {
+                float4_t xg[4], xu[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const bool in = s0 + u < ksplit;
+                    xg[u] = in ? *(const float4_t*)(g + (int64_t)(s0 + u) * plane) : (float4_t){0, 0, 0, 0};
+                    xu[u] = in ? *(const float4_t*)(g + (int64_t)(s0 + u) * plane + N) : (float4_t){0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    if (s0 + u < ksplit) {
+                        gg += xg[u];
+                        uu += xu[u];
+                    }
+            }
+            uint32_t hb[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                hb[t] = f32_to_bf16(silu_f(gg[t]) * uu[t]);
+                const uint32_t mag = hb[t] & 0x7FFFu;
+                hmax = hmax > mag ? hmax : mag;
+            }
+            *(u32x2*)(h + (int64_t)r * N + c) = (u32x2){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        }
+    } else
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / N, c = i - r * N;
@@ -2161,6 +2194,30 @@ swiglu_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t rows
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int64_t count, void* out, int out_bf16)
 {
+    if (count % 4 == 0 && ((uintptr_t)out & (out_bf16 ? 7 : 15)) == 0) {
+        // four consecutive outputs per thread, the planes' loads four at a
+        // time, added in split order
+        for (int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x); i < count;
+             i += 4 * (int64_t)gridDim.x * blockDim.x) {
+            float4_t v = *(const float4_t*)(partial + i);
+            for (int s0 = 1; s0 < ksplit; s0 += 4) {
+                float4_t x[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    x[u] = s0 + u < ksplit ? *(const float4_t*)(partial + (int64_t)(s0 + u) * count + i)
+                                           : (float4_t){0, 0, 0, 0};
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    if (s0 + u < ksplit)
+                        v += x[u];
+            }
+            if (out_bf16)
+                *(u32x2*)((uint16_t*)out + i) = (u32x2){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            else
+                *(float4_t*)((float*)out + i) = v;
+        }
+        return;
+    }
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x) {
         float v = partial[i];
