@@ -710,7 +710,7 @@ int mx_small_bm(int64_t T, int64_t I) { return (mx_all_small(T) && I % kMsBK == 
 
 // Workgroups of the MX streaming kernel the device holds at once (a multiple
 // of 8; one query per mode and device, cached as stream_resident caches).
-template <int MODE>
+template <int MODE, bool SC4>
 int64_t mx_stream_resident()
 {
     static std::atomic<int> cached[64];
@@ -720,7 +720,7 @@ int64_t mx_stream_resident()
     int v = cached[dev].load(std::memory_order_relaxed);
     if (v == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mx_stream_kernel<MODE>, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mx_stream_kernel<MODE, SC4>, 256, 0) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -745,8 +745,16 @@ nvfp4_status launch_mx_stream(MxArgs q, int64_t m_tiles_ub, hipStream_t st)
         return NVFP4_OK;
     if (items > 0x7FFFFFFF)
         return NVFP4_ERR_SHAPE;
-    const int64_t blocks = std::min(ceil_div(items, 8) * 8, mx_stream_resident<MODE>());
-    mx_stream_kernel<MODE><<<(unsigned)blocks, 256, 0, st>>>(q);
+    // scale bytes of four stages per request when every item holds whole
+    // four-stage chunks and the scale arrays are 16-byte aligned
+    const bool sc4 = q.K % (4 * kMsBK) == 0 && (((uintptr_t)q.w_sc | (uintptr_t)q.a_sc) & 15) == 0;
+    if (sc4) {
+        const int64_t blocks = std::min(ceil_div(items, 8) * 8, mx_stream_resident<MODE, true>());
+        mx_stream_kernel<MODE, true><<<(unsigned)blocks, 256, 0, st>>>(q);
+    } else {
+        const int64_t blocks = std::min(ceil_div(items, 8) * 8, mx_stream_resident<MODE, false>());
+        mx_stream_kernel<MODE, false><<<(unsigned)blocks, 256, 0, st>>>(q);
+    }
     return launch_status();
 }
 

@@ -393,14 +393,23 @@ constexpr int kMsBK = 256;   // K elements per stage
 constexpr int kMsBN = 128;   // W rows per workgroup
 constexpr int kMsBM = 32;    // A rows per tile
 
-template <int MODE>
+//
+// Scale bytes (SC4 = false): each of threads 0-159 loads its row's 8 bytes
+// of a stage.  SC4 (stages per item a multiple of 4, K % 1024 == 0, 16-byte
+// aligned scale arrays): the 32 bytes of four stages in one request (inside
+// one cache line), carried in the register set of the chunk's first stage
+// and stored, at that stage's LDS store, into one of two chunk buffers
+// (chunk parity) that the next four stages' MFMAs read.  Items hold whole
+// chunks, so chunk c is global stages [4 c, 4 c + 4) of the workgroup's walk.
+template <int MODE, bool SC4>
 __global__ void __launch_bounds__(256)
 mx_stream_kernel(MxArgs p)
 {
+    constexpr int SCW = SC4 ? 8 : 2;  // u32 scale words per row in one scale buffer
     __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][kMsBN * 128];  // E2M1 codes, 2 x 16 KB
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kMsBM * 256];  // E4M3, 2 x 8 KB
-    __shared__ __attribute__((aligned(16))) uint32_t lds_sw[2][kMsBN * 2];  // W scale bytes, 8 per row
-    __shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][kMsBM * 2];  // A scale bytes, 8 per row
+    __shared__ __attribute__((aligned(16))) uint32_t lds_sw[2][kMsBN * SCW];  // W scale bytes, 4 * SCW per row
+    __shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][kMsBM * SCW];  // A scale bytes, 4 * SCW per row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -487,7 +496,8 @@ mx_stream_kernel(MxArgs p)
     };
 
     u32x4 wreg[3][4], areg[3][2];
-    u32x2 sreg[3];
+    u32x2 sreg[3];            // (!SC4) a stage's 8 scale bytes
+    u32x4 slo[3], shi[3];     // (SC4) a chunk's 32 scale bytes, in its first stage's set
     const bool loads_sc = tid < kMsBN + kMsBM;
     auto load_stage = [&](int st, int set) {
 #pragma unroll
@@ -496,10 +506,18 @@ mx_stream_kernel(MxArgs p)
 #pragma unroll
         for (int j = 0; j < 2; j++)
             areg[set][j] = *(const u32x4*)(asrc[j] + (int64_t)st * kMsBK);
-        if (loads_sc)
+        if (SC4) {
+            if (loads_sc && (st & 3) == 0) {
+                const u32x4* src = (const u32x4*)(ssrc + (int64_t)st * (kMsBK / 32));
+                slo[set] = src[0];
+                shi[set] = src[1];
+            }
+        } else if (loads_sc) {
             sreg[set] = *(const u32x2*)(ssrc + (int64_t)st * (kMsBK / 32));
+        }
     };
-    auto store_stage = [&](int set, int b) {
+    // LDS store of the register set of global stage gs into stage buffer b
+    auto store_stage = [&](int set, int b, int gs) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int r = 32 * j + (tid >> 3);
@@ -510,20 +528,32 @@ mx_stream_kernel(MxArgs p)
             const int r = 16 * j + (tid >> 4);
             *(u32x4*)(&lds_a[b][r * 256 + 16 * ((tid & 15) ^ (r & 15))]) = areg[set][j];
         }
-        if (tid < kMsBN)
+        if (SC4) {
+            if ((gs & 3) == 0) {
+                const int cb = (gs >> 2) & 1;
+                if (tid < kMsBN) {
+                    *(u32x4*)(&lds_sw[cb][8 * tid]) = slo[set];
+                    *(u32x4*)(&lds_sw[cb][8 * tid + 4]) = shi[set];
+                } else if (loads_sc) {
+                    *(u32x4*)(&lds_sa[cb][8 * (tid - kMsBN)]) = slo[set];
+                    *(u32x4*)(&lds_sa[cb][8 * (tid - kMsBN) + 4]) = shi[set];
+                }
+            }
+        } else if (tid < kMsBN) {
             *(u32x2*)(&lds_sw[b][2 * tid]) = sreg[set];
-        else if (loads_sc)
+        } else if (loads_sc) {
             *(u32x2*)(&lds_sa[b][2 * (tid - kMsBN)]) = sreg[set];
+        }
     };
 
     float16_t acc = (float16_t){};
     // k-steps S = 0..3 of the stage in buffer b: the wave's W fragment row
     // fr of block 2 S + q (16 bytes of codes) and A row fr's elements
     // [16 q, +16) of blocks 2 S and 2 S + 1; scale byte 2 S + q of each row
-    auto compute = [&](int b) {
+    auto compute = [&](int b, int gs) {
         const int rw = 32 * wave + fr;
-        const uint32_t* swr = &lds_sw[b][2 * rw];
-        const uint32_t* sar = &lds_sa[b][2 * fr];
+        const uint32_t* swr = SC4 ? &lds_sw[(gs >> 2) & 1][8 * rw + 2 * (gs & 3)] : &lds_sw[b][2 * rw];
+        const uint32_t* sar = SC4 ? &lds_sa[(gs >> 2) & 1][8 * fr + 2 * (gs & 3)] : &lds_sa[b][2 * fr];
 #pragma unroll
         for (int S = 0; S < 4; S++) {
             const u32x4 w = *(const u32x4*)(&lds_w[b][rw * 128 + 16 * sk_wslot(rw, 2 * S + q)]);
@@ -604,15 +634,15 @@ mx_stream_kernel(MxArgs p)
     load_next(0);
     load_next(1);
     load_next(2);
-    store_stage(0, 0);
+    store_stage(0, 0, 0);
     __syncthreads();
     int g = 0;
     auto iter = [&](auto set_tag) {
         constexpr int cur = decltype(set_tag)::value;
         constexpr int nxt = (cur + 1) % 3;
-        store_stage(nxt, (g + 1) & 1);
+        store_stage(nxt, (g + 1) & 1, g + 1);
         load_next(cur);
-        compute(g & 1);
+        compute(g & 1, g);
         __syncthreads();
         g++;
         if (++c_s == nst) {

@@ -120,11 +120,13 @@ def test_mx_moe_decode_batch(orc):
 @pytest.mark.parametrize("cfg", [
     synth.MoE(seed=54, E=16, k=4, H=2048, I=512, T=48, zipf=1.1),  # 8 / 2 stages, experts of 1-45 rows
     synth.MoE(seed=55, E=8, k=2, H=512, I=256, T=1),               # one token
-], ids=["skewed-many-stages", "one-token"])
+    synth.MoE(seed=57, E=8, k=2, H=1024, I=1024, T=40),            # K % 1024 == 0 in both projections
+], ids=["skewed-many-stages", "one-token", "four-stage-scale-chunks"])
 def test_mx_moe_streaming_every_row(orc, cfg):
     """The streaming class with several 256-element stages per item (the
     register pipeline crosses items), experts holding more than one 32-row
-    tile, and a single token; every row checked."""
+    tile, a single token, and K a multiple of 1024 in both projections (the
+    scale bytes of four stages per request); every row checked."""
     _check_mx_moe(orc, cfg)
 
 
