@@ -34,10 +34,13 @@ def _mx_experts(cfg, which):
     return torch.stack(packed).contiguous(), torch.stack(e8).contiguous()
 
 
-def _check_mx_moe(orc, cfg, sample_rows=None, sample_tokens=None, seed=0, ids=None):
+def _check_mx_moe(orc, cfg, sample_rows=None, sample_tokens=None, seed=0, ids=None, experts=None):
     step(f"mx moe build E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} T={cfg.T}")
-    w13p, w13e = _mx_experts(cfg, "w13")
-    w2p, w2e = _mx_experts(cfg, "w2")
+    if experts is None:
+        w13p, w13e = _mx_experts(cfg, "w13")
+        w2p, w2e = _mx_experts(cfg, "w2")
+    else:
+        w13p, w13e, w2p, w2e = experts
     x = cfg.x(DEV)
     rids, w = workloads.routing(cfg, DEV)
     ids = rids if ids is None else ids.to(DEV)
@@ -136,6 +139,19 @@ def test_mx_moe_streaming_repeated_ids(orc):
     cfg = synth.MoE(seed=56, E=4, k=3, H=256, I=256, T=40)
     ids = torch.full((cfg.T, cfg.k), 1, dtype=torch.int32)
     _check_mx_moe(orc, cfg, ids=ids)
+
+
+def test_mx_moe_decode_full_size_sampled(orc):
+    """The 384-expert top-8 decode batch (T = 64) at its real shapes, H = 7168
+    and I = 2048 (page "DeepSeek-V4.1-Flash-NVFP4", sections 一 and 二: the
+    routed experts as stored in MXFP4), as the bench times it: every row in
+    32-row streaming tiles, both K multiples of 1024 (scale bytes of four
+    stages per request); sampled rows and tokens."""
+    cfg = synth.C4_DECODE
+    W = workloads.build_moe_weights(cfg, DEV, keep_mx=True)
+    experts = (W.mx13[0], W.mx13[1], W.mx2[0], W.mx2[1])
+    del W.w13, W.w2
+    _check_mx_moe(orc, cfg, sample_rows=48, sample_tokens=6, experts=experts)
 
 
 def test_mx_moe_repeated_ids_decode_batch(orc):
