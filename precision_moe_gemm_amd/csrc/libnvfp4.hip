@@ -1378,12 +1378,18 @@ nvfp4_status mx_moe_w4a8(const void* x, const int32_t* ids, const float* w, int6
     int32_t* plan = at<int32_t>(ws, L.plan);
     uint32_t* hmax = at<uint32_t>(ws, L.hmax);
     // 1. route (also zeroes the h max word); one tile plan serves both
-    // projections (64-row small tiles)
-    if ((s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st)) != NVFP4_OK)
-        return s;
-    moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, mx_small_bm(T, I), mx_all_small(T), plan);
-    if ((s = launch_status()) != NVFP4_OK)
-        return s;
+    // projections, written by the route's workgroup when the batch is small
+    if (np <= kRouteSmall) {
+        if ((s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st, plan, mx_small_bm(T, I),
+                            mx_all_small(T))) != NVFP4_OK)
+            return s;
+    } else {
+        if ((s = route_impl(ids, T, k, E, perm, offsets, inv, ws, L.r, hmax, st)) != NVFP4_OK)
+            return s;
+        moe_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, mx_small_bm(T, I), mx_all_small(T), plan);
+        if ((s = launch_status()) != NVFP4_OK)
+            return s;
+    }
     // 2. x -> MXFP8 (token order)
     if ((s = mxfp8_quantize(x, T, H, H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), stream)) != NVFP4_OK)
         return s;
