@@ -301,7 +301,9 @@ dequantize_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict
 // out[i] = dequantize(table row ids[i]) for i < n, rows of `hpr` half-blocks
 // (cols / 8); the same value rule as dequantize_kernel.  An id outside
 // [0, rows) gives a zero output row and raises NVFP4_ERR_RANGE.  Work item
-// = one output half-block; four per thread per trip, loads first.
+// = one output half-block; four per thread per trip, loads first.  Plain
+// stores: on the n-gram shard lookup they measured 4% faster than
+// nontemporal ones (the reverse of the contiguous dequantize).
 template <bool kBf16>
 __global__ void __launch_bounds__(kQuantThreads)
 gather_dequant_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
@@ -343,13 +345,12 @@ gather_dequant_kernel(const uint32_t* __restrict__ packed, const uint8_t* __rest
                 v[2 * t + 1] = ok[u] ? (q[t].y * sc) * G : 0.0f;
             }
             if (kBf16) {
-                __builtin_nontemporal_store((u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
-                                            (u32x4*)out + hb);
+                *((u32x4*)out + hb) = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
             } else {
                 float4_t* o = (float4_t*)out + 2 * (int64_t)hb;
-                __builtin_nontemporal_store((float4_t){v[0], v[1], v[2], v[3]}, o);
-                __builtin_nontemporal_store((float4_t){v[4], v[5], v[6], v[7]}, o + 1);
+                o[0] = (float4_t){v[0], v[1], v[2], v[3]};
+                o[1] = (float4_t){v[4], v[5], v[6], v[7]};
             }
         }
     }
