@@ -1068,7 +1068,10 @@ gemm_tile_kernel(GemmArgs p)
 // every wave row in this wave's own LDS region (TM rows; 16-byte slot s of row
 // r at slot s ^ (r % 8)) and writes whole 16-byte pieces: 8 lanes per row, 8
 // rows per store instruction (gate_up with 64-column wave tiles: 4 lanes per
-// row of 32 h columns, 16 rows).
+// row of 32 h columns, 16 rows).  The output is not read again by this
+// launch: nontemporal stores, so that a round's output (4-8 MB per XCD)
+// does not push out the operand lines the resident tiles share in L2
+// (384-expert prefill: down 3108 -> 2985 us, gate_up 5159 -> 5115 us).
 template <int BN, int TM, int TN, int FM, int FN, int MODE>
 NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float16_t (&acc)[FM][FN], int wave_m,
                             int wave_n, int lane, uint8_t* stg)
@@ -1142,7 +1145,8 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
             for (int k = 0; k < TM / RPI; k++) {
                 const int r = RPI * k + hr;
                 if (r < rows_left)
-                    *(u32x4*)(h + (wrow0 + r) * N + hcol0 + 8 * hs) = *(const u32x4*)slot(r, hs);
+                    __builtin_nontemporal_store(*(const u32x4*)slot(r, hs),
+                                                (u32x4*)(h + (wrow0 + r) * N + hcol0 + 8 * hs));
             }
             // one atomic per workgroup: the four waves meet in LDS first
             __shared__ uint32_t red[16];
@@ -1179,7 +1183,7 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
                         const u32x4 v = *(const u32x4*)slot(r, sl);
                         uint16_t* dst = ob + (wrow0 + r) * N + col;
                         if (vec) {
-                            *(u32x4*)dst = v;
+                            __builtin_nontemporal_store(v, (u32x4*)dst);
                         } else {
                             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1215,7 +1219,7 @@ NVFP4_DEV void store_tile_t(const GemmArgs& p, const TileCoord& tc, const float1
                         const float4_t v = *(const float4_t*)slot(r, sl);
                         float* dst = of + (wrow0 + r) * N + col;
                         if (vec) {
-                            *(float4_t*)dst = v;
+                            __builtin_nontemporal_store(v, (float4_t*)dst);
                         } else {
 #pragma unroll
                             for (int t = 0; t < 4; t++)
