@@ -174,3 +174,30 @@ def test_mx_moe_unsupported_shapes():
     with pytest.raises(nv.NVFP4Error) as ei:  # H % 256 != 0
         nv.mx_moe_w4a8(x, ids, w, w13, w13e, w2, w2e)
     assert ei.value.status == 6
+
+
+def test_mx_moe_empty_deterministic_and_bad_ids():
+    """No tokens gives an empty output; two calls give the same bytes; an
+    expert id outside [0, E) raises the range error and its pair is dropped
+    (the output stays finite)."""
+    cfg = synth.MoE(seed=58, E=4, k=2, H=512, I=256, T=24)
+    w13p, w13e = _mx_experts(cfg, "w13")
+    w2p, w2e = _mx_experts(cfg, "w2")
+    x = cfg.x(DEV)
+    ids, w = workloads.routing(cfg, DEV)
+    step("mx moe empty / deterministic / bad ids")
+    a = nv.mx_moe_w4a8(x, ids, w, w13p, w13e, w2p, w2e)
+    b = nv.mx_moe_w4a8(x, ids, w, w13p, w13e, w2p, w2e)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    e = nv.mx_moe_w4a8(x[:0], ids[:0], w[:0], w13p, w13e, w2p, w2e)
+    assert e.shape == (0, cfg.H)
+    assert nv.nvfp4_get_error() == 0
+    bad = ids.clone()
+    bad[2, 1] = cfg.E
+    bad[7, 0] = -3
+    c = nv.mx_moe_w4a8(x, bad, w, w13p, w13e, w2p, w2e)
+    torch.cuda.synchronize()
+    assert nv.nvfp4_get_error() == 3
+    assert torch.isfinite(c.float()).all()
+    assert nv.nvfp4_get_error() == 0

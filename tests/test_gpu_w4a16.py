@@ -139,3 +139,29 @@ def test_w4a16_moe_384_experts_decode_sampled(orc):
     g2 = nv.NVFP4Tensor(W.w2.packed, W.w2.scales, W.w2.global_, W.w2.rows, W.w2.cols, W.w2.batch, 0)
     step("w4a16 moe general-scale path")
     assert torch.equal(nv.nvfp4_moe_w4a16(x, ids, w, g13, g2), out)
+
+
+def test_w4a16_moe_empty_deterministic_and_bad_ids():
+    """No tokens gives an empty output; two calls give the same bytes; an
+    expert id outside [0, E) raises the range error and its pair is dropped
+    (the output stays finite)."""
+    cfg = synth.MoE(seed=59, E=4, k=2, H=512, I=256, T=24)
+    W = workloads.build_moe_weights(cfg, DEV)
+    x = cfg.x(DEV)
+    ids, w = workloads.routing(cfg, DEV)
+    step("w4a16 moe empty / deterministic / bad ids")
+    a = nv.nvfp4_moe_w4a16(x, ids, w, W.w13, W.w2)
+    b = nv.nvfp4_moe_w4a16(x, ids, w, W.w13, W.w2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    e = nv.nvfp4_moe_w4a16(x[:0], ids[:0], w[:0], W.w13, W.w2)
+    assert e.shape == (0, cfg.H)
+    assert nv.nvfp4_get_error() == 0
+    bad = ids.clone()
+    bad[2, 1] = cfg.E
+    bad[7, 0] = -3
+    c = nv.nvfp4_moe_w4a16(x, bad, w, W.w13, W.w2)
+    torch.cuda.synchronize()
+    assert nv.nvfp4_get_error() == 3
+    assert torch.isfinite(c.float()).all()
+    assert nv.nvfp4_get_error() == 0
